@@ -1,0 +1,312 @@
+// Host side of the C ABI: validation, the 2D / split-KV dispatcher and launches.
+//
+// The dispatcher follows the pages' rule (AITER PR #3962, section "Changes";
+// RocKE README, "Why three tables"): stay one-pass when the one-pass grid
+// already fills the device or the visible key range is short; otherwise split
+// each query block's (window-bounded) key range into partitions so the grid
+// fills the device.  Partitions are sized per query block on the device so
+// that n_part of them always cover the block's whole visible range (the
+// capped-partition defect of AITER PR #3962's review cannot occur), and it uses
+// host integers only (max_seqlen_q / max_seqlen_k), never a device sync.
+
+#include <cmath>
+#include <cstring>
+
+#include "ua_internal.h"
+
+using namespace ua;
+
+namespace {
+
+struct Hasher {
+  uint64_t h = 1469598103934665603ull;  // FNV-1a 64
+  template <typename T>
+  void add(const T& v) {
+    const unsigned char* b = reinterpret_cast<const unsigned char*>(&v);
+    for (size_t i = 0; i < sizeof(T); ++i) {
+      h ^= b[i];
+      h *= 1099511628211ull;
+    }
+  }
+};
+
+uint64_t problem_hash(const ua_problem* p) {
+  Hasher hs;
+  hs.add(p->num_seqs); hs.add(p->total_q); hs.add(p->num_q_heads); hs.add(p->num_kv_heads);
+  hs.add(p->head_dim); hs.add(p->block_size); hs.add(p->num_blocks);
+  hs.add(p->max_blocks_per_seq); hs.add(p->max_seqlen_q); hs.add(p->max_seqlen_k);
+  hs.add(p->q_dtype); hs.add(p->kv_dtype); hs.add(p->o_dtype); hs.add(p->scale);
+  hs.add(p->softcap); hs.add(p->window); hs.add(p->k_scale); hs.add(p->v_scale);
+  hs.add(p->has_alibi); hs.add(p->has_sinks); hs.add(p->q_stride_tok); hs.add(p->q_stride_head);
+  hs.add(p->o_stride_tok); hs.add(p->o_stride_head); hs.add(p->kv_stride_block);
+  hs.add(p->kv_stride_slot); hs.add(p->kv_stride_head);
+  return hs.h;
+}
+
+int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+bool is_16bit(int32_t t) { return t == UA_F16 || t == UA_BF16; }
+
+ua_status validate(const ua_problem* p) {
+  if (!p) return UA_EINVAL;
+  if (p->num_seqs < 0 || p->total_q < 0) return UA_EINVAL;
+  if (p->num_q_heads <= 0 || p->num_kv_heads <= 0) return UA_EINVAL;
+  if (p->num_q_heads % p->num_kv_heads != 0) return UA_EINVAL;
+  if (p->block_size <= 0 || p->num_blocks < 0) return UA_EINVAL;
+  if (p->max_seqlen_q < 0 || p->max_seqlen_k < 0 || p->max_seqlen_q > p->max_seqlen_k)
+    return UA_EINVAL;
+  if (p->max_seqlen_k > 0 && p->num_blocks == 0) return UA_EINVAL;
+  if (p->max_blocks_per_seq < 0 || p->max_blocks_per_seq < ceil_div(p->max_seqlen_k, p->block_size))
+    return UA_EINVAL;
+  if (p->num_seqs > 0 && p->total_q > (int64_t)p->num_seqs * p->max_seqlen_q) return UA_EINVAL;
+  if (!std::isfinite(p->scale) || !std::isfinite(p->softcap)) return UA_EINVAL;
+  if (!is_16bit(p->q_dtype)) return UA_EUNSUPPORTED;
+  if (p->kv_dtype != p->q_dtype && p->kv_dtype != UA_FP8_E4M3FN) return UA_EUNSUPPORTED;
+  if (p->o_dtype != p->q_dtype) return UA_EUNSUPPORTED;
+  if (p->kv_dtype == UA_FP8_E4M3FN) {
+    if (!std::isfinite(p->k_scale) || !std::isfinite(p->v_scale) || p->k_scale <= 0.f ||
+        p->v_scale <= 0.f)
+      return UA_EINVAL;
+  }
+  if (p->head_dim != 64 && p->head_dim != 128 && p->head_dim != 256) return UA_EUNSUPPORTED;
+  if ((int64_t)p->total_q * p->num_q_heads >= (int64_t)1 << 31) return UA_EUNSUPPORTED;
+  if (p->q_stride_tok <= 0 || p->q_stride_head <= 0 || p->o_stride_tok <= 0 ||
+      p->o_stride_head <= 0 || p->kv_stride_block <= 0 || p->kv_stride_slot <= 0 ||
+      p->kv_stride_head <= 0)
+    return UA_EINVAL;
+  // 16-byte vector access: strides in whole 16-byte units.
+  const int64_t kv_vec = p->kv_dtype == UA_FP8_E4M3FN ? 16 : 8;
+  if (p->q_stride_tok % 8 || p->q_stride_head % 8 || p->o_stride_tok % 8 || p->o_stride_head % 8)
+    return UA_EUNSUPPORTED;
+  if (p->kv_stride_block % kv_vec || p->kv_stride_slot % kv_vec || p->kv_stride_head % kv_vec)
+    return UA_EUNSUPPORTED;
+  const int G = p->num_q_heads / p->num_kv_heads;
+  if (G > kSmallRows) return UA_EUNSUPPORTED;
+  return UA_OK;
+}
+
+ua_status check_args(const ua_problem* p, const ua_args* a) {
+  if (!a) return UA_EINVAL;
+  if (p->total_q == 0 || p->num_seqs == 0) return UA_OK;
+  if (!a->q || !a->k_cache || !a->v_cache || !a->block_table || !a->cu_seqlens_q ||
+      !a->seq_lens || !a->out)
+    return UA_EINVAL;
+  if ((p->has_alibi != 0) != (a->alibi_slopes != nullptr)) return UA_EINVAL;
+  if ((p->has_sinks != 0) != (a->sinks != nullptr)) return UA_EINVAL;
+  auto aligned = [](const void* ptr, uintptr_t n) { return ((uintptr_t)ptr % n) == 0; };
+  if (!aligned(a->q, 16) || !aligned(a->out, 16) || !aligned(a->k_cache, 16) ||
+      !aligned(a->v_cache, 16))
+    return UA_EUNSUPPORTED;
+  return UA_OK;
+}
+
+uint64_t ml_bytes(const ua_problem* p, int n_part) {
+  return 2ull * n_part * (uint64_t)p->total_q * p->num_q_heads * 4ull;
+}
+
+uint64_t acc_offset(const ua_problem* p, int n_part) {
+  return (ml_bytes(p, n_part) + 255ull) & ~255ull;
+}
+
+Params make_params(const ua_problem* p, const ua_plan_t* plan, const ua_args* a, void* ws) {
+  Params q;
+  std::memset(&q, 0, sizeof(q));
+  q.q = a->q;
+  q.k = a->k_cache;
+  q.v = a->v_cache;
+  q.block_table = a->block_table;
+  q.cu_seqlens_q = a->cu_seqlens_q;
+  q.seq_lens = a->seq_lens;
+  q.alibi = a->alibi_slopes;
+  q.sinks = a->sinks;
+  q.out = a->out;
+  q.lse = a->lse;
+  if (ws) {
+    const int64_t R = (int64_t)p->total_q * p->num_q_heads;
+    char* base = reinterpret_cast<char*>(ws);
+    q.ws_m = reinterpret_cast<float*>(base);
+    q.ws_l = reinterpret_cast<float*>(base + (uint64_t)plan->n_part * R * 4);
+    q.ws_acc = reinterpret_cast<float*>(base + acc_offset(p, plan->n_part));
+  }
+  q.q_stride_tok = p->q_stride_tok;
+  q.q_stride_head = p->q_stride_head;
+  q.o_stride_tok = p->o_stride_tok;
+  q.o_stride_head = p->o_stride_head;
+  q.kv_stride_block = p->kv_stride_block;
+  q.kv_stride_slot = p->kv_stride_slot;
+  q.kv_stride_head = p->kv_stride_head;
+  q.num_seqs = p->num_seqs;
+  q.total_q = p->total_q;
+  q.num_q_heads = p->num_q_heads;
+  q.num_kv_heads = p->num_kv_heads;
+  q.group = p->num_q_heads / p->num_kv_heads;
+  q.block_size = p->block_size;
+  q.max_blocks_per_seq = p->max_blocks_per_seq;
+  q.bs_div = make_fastdiv((uint32_t)p->block_size);
+  q.block_q = plan->block_q;
+  q.n_part = plan->n_part;
+  q.window = p->window > 0 ? p->window : 0;
+  int trips = 0;
+  while ((1 << trips) < p->num_seqs + 1) ++trips;
+  q.search_trips = trips;
+  const bool fp8 = p->kv_dtype == UA_FP8_E4M3FN;
+  const float ks = fp8 ? p->k_scale : 1.0f;
+  const double log2e = 1.4426950408889634;
+  q.qk_scale2 = (float)((double)p->scale * ks * log2e);
+  q.softcap_on = p->softcap > 0.f ? 1 : 0;
+  if (q.softcap_on) {
+    q.cap_in = (float)((double)p->scale * ks / p->softcap);
+    q.cap_out2 = (float)((double)p->softcap * log2e);
+  }
+  q.v_scale = fp8 ? p->v_scale : 1.0f;
+  q.grid_x = plan->grid_x;
+  return q;
+}
+
+}  // namespace
+
+extern "C" {
+
+int32_t ua_abi_version(void) { return UA_ABI_VERSION; }
+
+const char* ua_status_string(int32_t s) {
+  switch (s) {
+    case UA_OK: return "ok";
+    case UA_EINVAL: return "invalid argument";
+    case UA_EUNSUPPORTED: return "unsupported configuration";
+    case UA_EWORKSPACE: return "workspace missing or too small";
+    case UA_EHIP: return "HIP launch error";
+    case UA_EPLAN: return "plan does not match the problem or the call";
+    default: return "unknown status";
+  }
+}
+
+ua_status ua_plan(const ua_problem* prob, int32_t num_cus, int32_t force_path,
+                  int32_t force_n_part, ua_plan_t* plan) {
+  if (!plan) return UA_EINVAL;
+  ua_status st = validate(prob);
+  if (st != UA_OK) return st;
+  if (force_path != UA_PATH_AUTO && force_path != UA_PATH_2D && force_path != UA_PATH_SPLITKV)
+    return UA_EINVAL;
+  if (force_n_part < 0 || force_n_part > 65535) return UA_EINVAL;
+  if (force_path == UA_PATH_2D && force_n_part > 1) return UA_EINVAL;
+  if (num_cus <= 0) num_cus = 256;
+  std::memset(plan, 0, sizeof(*plan));
+  const int G = prob->num_q_heads / prob->num_kv_heads;
+  plan->kernel = 0;
+  plan->block_q = kSmallRows / G;
+  const int bq = plan->block_q;
+  const int64_t slots = prob->num_seqs > 0 ? (int64_t)prob->total_q / bq + prob->num_seqs : 0;
+  const int64_t est_blocks =
+      std::min<int64_t>(slots, (int64_t)prob->num_seqs * ceil_div(prob->max_seqlen_q, bq));
+  int64_t eff_k = prob->max_seqlen_k;
+  if (prob->window > 0) eff_k = std::min<int64_t>(eff_k, (int64_t)prob->window + bq - 1);
+  const int64_t wgs = est_blocks * prob->num_kv_heads;
+
+  // Automatic partition count: fill about four small workgroups per CU,
+  // keep at least 256 keys per partition, and stay one-pass for short ranges.
+  int auto_parts = 1;
+  if (wgs > 0 && eff_k > 1024) {
+    const int64_t want = ceil_div(4ll * num_cus, wgs);
+    const int64_t by_len = std::max<int64_t>(1, eff_k / 256);
+    auto_parts = (int)std::max<int64_t>(1, std::min<int64_t>(std::min(want, by_len), 64));
+  }
+  int n_part;
+  if (force_path == UA_PATH_2D) {
+    n_part = 1;
+    plan->path = UA_PATH_2D;
+  } else if (force_path == UA_PATH_SPLITKV) {
+    n_part = force_n_part > 0 ? force_n_part : auto_parts;
+    plan->path = UA_PATH_SPLITKV;
+  } else {
+    n_part = force_n_part > 0 ? force_n_part : auto_parts;
+    plan->path = n_part > 1 ? UA_PATH_SPLITKV : UA_PATH_2D;
+  }
+  plan->n_part = n_part;
+  if (slots > 0x7fffffff) return UA_EUNSUPPORTED;
+  plan->grid_x = (int32_t)slots;
+  plan->grid_y = prob->num_kv_heads;
+  plan->grid_z = n_part;
+  plan->workspace_bytes =
+      plan->path == UA_PATH_SPLITKV
+          ? acc_offset(prob, n_part) +
+                (uint64_t)n_part * prob->total_q * prob->num_q_heads * prob->head_dim * 4ull
+          : 0;
+  plan->problem_hash = problem_hash(prob);
+  return UA_OK;
+}
+
+uint64_t ua_workspace_acc_offset(const ua_problem* prob, const ua_plan_t* plan) {
+  if (!prob || !plan) return 0;
+  return acc_offset(prob, plan->n_part);
+}
+
+static ua_status check_plan(const ua_problem* prob, const ua_plan_t* plan, int32_t path) {
+  if (!prob || !plan) return UA_EINVAL;
+  ua_status st = validate(prob);
+  if (st != UA_OK) return st;
+  if (plan->problem_hash != problem_hash(prob) || plan->path != path) return UA_EPLAN;
+  if (plan->n_part < 1 || plan->block_q < 1) return UA_EPLAN;
+  return UA_OK;
+}
+
+static ua_status launch_main(const ua_problem* prob, const ua_plan_t* plan, const Params& q,
+                             bool split, void* stream) {
+  dim3 grid((unsigned)plan->grid_x, (unsigned)plan->grid_y, (unsigned)plan->grid_z);
+  const int fp8 = prob->kv_dtype == UA_FP8_E4M3FN;
+  hipError_t e = plan->kernel == 0
+                     ? launch_small(q, prob->q_dtype, fp8, prob->head_dim, split, grid,
+                                    (hipStream_t)stream)
+                     : launch_large(q, prob->q_dtype, fp8, prob->head_dim, split, grid,
+                                    (hipStream_t)stream);
+  return e == hipSuccess ? UA_OK : UA_EHIP;
+}
+
+ua_status ua_forward_2d(const ua_problem* prob, const ua_plan_t* plan, const ua_args* args,
+                        void* stream) {
+  ua_status st = check_plan(prob, plan, UA_PATH_2D);
+  if (st != UA_OK) return st;
+  if ((st = check_args(prob, args)) != UA_OK) return st;
+  if (prob->total_q == 0 || prob->num_seqs == 0) return UA_OK;
+  Params q = make_params(prob, plan, args, nullptr);
+  return launch_main(prob, plan, q, false, stream);
+}
+
+ua_status ua_forward_splitkv(const ua_problem* prob, const ua_plan_t* plan, const ua_args* args,
+                             void* workspace, size_t workspace_bytes, void* stream) {
+  ua_status st = check_plan(prob, plan, UA_PATH_SPLITKV);
+  if (st != UA_OK) return st;
+  if ((st = check_args(prob, args)) != UA_OK) return st;
+  if (prob->total_q == 0 || prob->num_seqs == 0) return UA_OK;
+  if (!workspace || workspace_bytes < plan->workspace_bytes || ((uintptr_t)workspace % 256))
+    return UA_EWORKSPACE;
+  Params q = make_params(prob, plan, args, workspace);
+  return launch_main(prob, plan, q, true, stream);
+}
+
+ua_status ua_reduce(const ua_problem* prob, const ua_plan_t* plan, const ua_args* args,
+                    const void* workspace, size_t workspace_bytes, void* stream) {
+  ua_status st = check_plan(prob, plan, UA_PATH_SPLITKV);
+  if (st != UA_OK) return st;
+  if (!args) return UA_EINVAL;
+  if (prob->total_q == 0 || prob->num_seqs == 0) return UA_OK;
+  if (!args->out) return UA_EINVAL;
+  if ((prob->has_sinks != 0) != (args->sinks != nullptr)) return UA_EINVAL;
+  if (((uintptr_t)args->out % 16)) return UA_EUNSUPPORTED;
+  if (!workspace || workspace_bytes < plan->workspace_bytes || ((uintptr_t)workspace % 256))
+    return UA_EWORKSPACE;
+  Params q = make_params(prob, plan, args, const_cast<void*>(workspace));
+  hipError_t e = launch_reduce(q, prob->o_dtype, prob->head_dim, (hipStream_t)stream);
+  return e == hipSuccess ? UA_OK : UA_EHIP;
+}
+
+ua_status ua_forward(const ua_problem* prob, const ua_plan_t* plan, const ua_args* args,
+                     void* workspace, size_t workspace_bytes, void* stream) {
+  if (!plan) return UA_EINVAL;
+  if (plan->path == UA_PATH_2D) return ua_forward_2d(prob, plan, args, stream);
+  ua_status st = ua_forward_splitkv(prob, plan, args, workspace, workspace_bytes, stream);
+  if (st != UA_OK) return st;
+  return ua_reduce(prob, plan, args, workspace, workspace_bytes, stream);
+}
+
+}  // extern "C"

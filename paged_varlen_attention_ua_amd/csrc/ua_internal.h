@@ -1,0 +1,82 @@
+// Internal definitions shared by the host planner and the gfx950 kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "../../include/ua.h"
+
+namespace ua {
+
+// Largest query group a small-block kernel packs into its 16 MFMA rows.
+constexpr int kSmallRows = 16;
+// Rows of a large (prefill) query block and its waves.
+constexpr int kLargeRows = 128;
+constexpr int kLargeWaves = 4;
+// Keys per inner tile of the small-block kernel (two 16-key MFMA blocks).
+constexpr int kSmallTile = 32;
+// Keys per inner tile of the large-block kernel.
+constexpr int kLargeTile = 64;
+// Waves per small-block workgroup; they split the key range of one block.
+constexpr int kSmallWaves = 4;
+
+// Division by a run-time invariant divisor with one multiply-high
+// (Granlund & Montgomery, "Division by Invariant Integers using
+// Multiplication", PLDI 1994, section 4): for d >= 1, l = ceil(log2 d),
+// m = floor(2^32 (2^l - d) / d) + 1; then n / d = (umulhi(n, m) + n) >> l
+// for every 32-bit n.
+struct FastDiv {
+  uint32_t d, m, l;
+};
+
+inline FastDiv make_fastdiv(uint32_t d) {
+  FastDiv f;
+  f.d = d;
+  uint32_t l = 0;
+  while ((1ull << l) < d) ++l;
+  f.l = l;
+  f.m = (uint32_t)((((1ull << l) - d) << 32) / d + 1);
+  return f;
+}
+
+// Everything a kernel launch needs, passed by value.
+struct Params {
+  const void* q;
+  const void* k;
+  const void* v;
+  const int32_t* block_table;
+  const int32_t* cu_seqlens_q;
+  const int32_t* seq_lens;
+  const float* alibi;  // [Hq] or null
+  const float* sinks;  // [Hq] or null
+  void* out;
+  float* lse;  // [total_q, Hq] or null
+  float* ws_m;
+  float* ws_l;
+  float* ws_acc;
+  int64_t q_stride_tok, q_stride_head;
+  int64_t o_stride_tok, o_stride_head;
+  int64_t kv_stride_block, kv_stride_slot, kv_stride_head;
+  int32_t num_seqs, total_q, num_q_heads, num_kv_heads, group;
+  int32_t block_size, max_blocks_per_seq;
+  FastDiv bs_div;
+  int32_t block_q;      // query tokens per query block
+  int32_t n_part;       // partitions (1 = one pass)
+  int32_t window;       // <= 0: off
+  int32_t search_trips; // ceil(log2(num_seqs + 1))
+  float qk_scale2;      // scale * k_scale * log2(e): raw dot -> base-2 logit
+  float cap_in;         // scale * k_scale / softcap (softcap on)
+  float cap_out2;       // softcap * log2(e)
+  float v_scale;        // fp8 value scale (1 otherwise)
+  int32_t softcap_on;
+  int32_t grid_x;       // number of query-block slots launched along x
+};
+
+// Launchers (defined next to their kernels).  Return hipError_t of the launch.
+hipError_t launch_small(const Params& p, int q_dtype, int kv_fp8, int head_dim, bool split,
+                        dim3 grid, hipStream_t stream);
+hipError_t launch_large(const Params& p, int q_dtype, int kv_fp8, int head_dim, bool split,
+                        dim3 grid, hipStream_t stream);
+hipError_t launch_reduce(const Params& p, int o_dtype, int head_dim, hipStream_t stream);
+
+}  // namespace ua

@@ -1,0 +1,87 @@
+// Split-KV reduce for gfx950: merges the per-partition softmax states.
+//
+// For each query row (token, head): M = max over partitions with l > 0 (and
+// the sink, in base 2), L = sum l_p 2^(m_p - M) + 2^(sink - M),
+// out = v_scale * sum acc_p 2^(m_p - M) / L; a row no partition saw is written
+// as zeros (AITER PR #3962, sections "Summary" and review reply: partitions
+// with l = 0 are skipped, their acc is never read, rows without keys return
+// zeros).  HBM-bound: each partition's acc row is read once with 16-byte loads.
+
+#include "ua_device.h"
+
+namespace ua {
+namespace {
+
+template <int OT, int D>
+__global__ __launch_bounds__(256) void reduce_kernel(Params p) {
+  constexpr int TPR = D / 4;            // threads per row, 4 values each
+  constexpr int RPB = 256 / TPR;        // rows per block
+  const int R = p.total_q * p.num_q_heads;
+  const int tid = threadIdx.x;
+  const int64_t row = (int64_t)blockIdx.x * RPB + tid / TPR;
+  const int d0 = (tid % TPR) * 4;
+  if (row >= R) return;
+  const int h = (int)(row % p.num_q_heads);
+  const int P = p.n_part;
+
+  float M = -INFINITY;
+  for (int q = 0; q < P; ++q) {
+    const float l = p.ws_l[(int64_t)q * R + row];
+    if (l > 0.0f) M = fmaxf(M, p.ws_m[(int64_t)q * R + row]);
+  }
+  const float sink2 = (p.sinks != nullptr) ? p.sinks[h] * kLog2e : -INFINITY;
+  const float Mt = fmaxf(M, sink2);
+  const float Ms = (Mt == -INFINITY) ? 0.0f : Mt;
+  float L = 0.0f;
+  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+  for (int q = 0; q < P; ++q) {
+    const float l = p.ws_l[(int64_t)q * R + row];
+    if (l > 0.0f) {
+      const float w = fast_exp2(p.ws_m[(int64_t)q * R + row] - Ms);
+      L += w * l;
+      const f32x4 a = *reinterpret_cast<const f32x4*>(p.ws_acc + ((int64_t)q * R + row) * D + d0);
+      acc += w * a;
+    }
+  }
+  const bool any_key = L > 0.0f;
+  if (sink2 != -INFINITY) L += fast_exp2(sink2 - Ms);
+  const float inv = any_key ? p.v_scale / L : 0.0f;
+  const int64_t tok = row / p.num_q_heads;
+  char* dst = reinterpret_cast<char*>(p.out) +
+              (tok * p.o_stride_tok + (int64_t)h * p.o_stride_head + d0) * 2;
+  *reinterpret_cast<u32x2*>(dst) =
+      u32x2{pack2<OT>(acc[0] * inv, acc[1] * inv), pack2<OT>(acc[2] * inv, acc[3] * inv)};
+  if (p.lse != nullptr && d0 == 0) p.lse[row] = (L > 0.0f) ? (Ms + fast_log2(L)) * kLn2 : -INFINITY;
+}
+
+template <int OT>
+hipError_t launch_reduce_t(const Params& p, int head_dim, hipStream_t stream) {
+  const int64_t R = (int64_t)p.total_q * p.num_q_heads;
+  if (R == 0) return hipSuccess;
+  switch (head_dim) {
+    case 64:
+      hipLaunchKernelGGL((reduce_kernel<OT, 64>), dim3((unsigned)((R + 15) / 16)), dim3(256), 0,
+                         stream, p);
+      break;
+    case 128:
+      hipLaunchKernelGGL((reduce_kernel<OT, 128>), dim3((unsigned)((R + 7) / 8)), dim3(256), 0,
+                         stream, p);
+      break;
+    case 256:
+      hipLaunchKernelGGL((reduce_kernel<OT, 256>), dim3((unsigned)((R + 3) / 4)), dim3(256), 0,
+                         stream, p);
+      break;
+    default:
+      return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_reduce(const Params& p, int o_dtype, int head_dim, hipStream_t stream) {
+  return o_dtype == UA_F16 ? launch_reduce_t<UA_F16>(p, head_dim, stream)
+                           : launch_reduce_t<UA_BF16>(p, head_dim, stream);
+}
+
+}  // namespace ua

@@ -1,0 +1,436 @@
+// Small-query-block attention kernel for gfx950: decode and split-KV partitions.
+//
+// One workgroup owns (query block, kv head, key partition).  A query block is
+// block_q consecutive query tokens of one sequence times the G = Hq / Hkv query
+// heads that share the kv head (grouped-query packing: every row of the block
+// reads the same K/V rows), at most 16 rows: the N side of a 16x16x32 MFMA.
+// The four waves of the workgroup walk interleaved 32-key tiles of the
+// partition, each keeping its own online-softmax state (running max m, sum l
+// and output accumulator, AITER PR #3962 review diff), and merge through LDS at
+// the end.  With one partition the block writes the final rows (the one-pass
+// form of the RocKE README, "Why three tables"); otherwise it writes the
+// partition's (m, l, acc) for ua_reduce.
+//
+// Data flow per 32-key tile and wave (no LDS in the loop):
+//   * K rows go straight from HBM into registers already in the MFMA A-operand
+//     layout (lane l: key l % 16, a contiguous quarter of the head dim), and
+//     S^T = K Q^T comes out with one query row per lane (row = l % 16).
+//   * Because P^T then sits in the B-operand layout of O^T = V^T P^T, P stays
+//     in registers; the eight keys a lane contributes are the ones its S^T
+//     accumulator holds.
+//   * V is loaded as whole 16-byte row pieces (four full rows per load
+//     instruction) and the per-lane transposition the A operand needs is done
+//     with byte permutes in registers.
+//   * Logits are kept in the base-2 domain (pre-multiplied by log2 e, exp2 for
+//     the exponentials), the README's convention (section "2D vs 2D").
+
+#include "ua_device.h"
+
+namespace ua {
+namespace {
+
+// Load N dwords (N in {1, 2, 4, 8}) from a 4*N-byte aligned address.
+template <int N>
+__device__ __forceinline__ void load_dw(const char* ptr, uint32_t* dst) {
+  if constexpr (N == 1) {
+    dst[0] = *reinterpret_cast<const uint32_t*>(ptr);
+  } else if constexpr (N == 2) {
+    u32x2 v = *reinterpret_cast<const u32x2*>(ptr);
+    dst[0] = v[0];
+    dst[1] = v[1];
+  } else {
+#pragma unroll
+    for (int i = 0; i < N / 4; ++i) {
+      u32x4 v = *reinterpret_cast<const u32x4*>(ptr + 16 * i);
+      dst[4 * i + 0] = v[0];
+      dst[4 * i + 1] = v[1];
+      dst[4 * i + 2] = v[2];
+      dst[4 * i + 3] = v[3];
+    }
+  }
+}
+
+template <int QT, bool FP8, int D>
+struct SmallCfg {
+  static constexpr int E = D / 16;         // head-dim values per lane per V row = PV MFMAs per tile
+  static constexpr int QC = D / 32;        // QK MFMAs per 16 keys
+  static constexpr int DQ = D / 4;         // head-dim values per lane per K/Q row
+  static constexpr int EB = FP8 ? 1 : 2;   // bytes per stored K/V element
+  static constexpr int KW = DQ * EB / 4;   // dwords per lane per K row
+  static constexpr int VW = E * EB / 4 > 0 ? E * EB / 4 : 1;  // dwords per lane per V row
+};
+
+template <int QT, bool FP8, int D>
+struct Tile {
+  using C = SmallCfg<QT, FP8, D>;
+  uint32_t k[2][C::KW];
+  uint32_t v[8][C::VW];
+};
+
+template <int QT, bool FP8, int D, bool PAGE16>
+__device__ __forceinline__ void load_tile(Tile<QT, FP8, D>& t, const Params& p,
+                                          const int32_t* __restrict__ bt_row,
+                                          const char* kbase, const char* vbase, int kt, int kl,
+                                          int k1, int g, int r16) {
+  using C = SmallCfg<QT, FP8, D>;
+  const int64_t slot_b = p.kv_stride_slot * C::EB;
+  const int64_t blk_b = p.kv_stride_block * C::EB;
+#pragma unroll
+  for (int hb = 0; hb < 2; ++hb) {
+    const int kb0 = kt + 16 * hb;
+    if constexpr (PAGE16) {
+      // block_size % 16 == 0: the 16 keys of this half share one cache block.
+      const bool live = (kb0 < k1) && (kb0 + 16 > kl);
+      int64_t off = 0;
+      if (live) {
+        const uint32_t bi = fastdiv((uint32_t)kb0, p.bs_div);
+        const int slot0 = kb0 - (int)bi * p.block_size;
+        off = (int64_t)bt_row[bi] * blk_b + (int64_t)slot0 * slot_b;
+      }
+      {
+        const int key = kb0 + r16;
+        if (live && key >= kl && key < k1)
+          load_dw<C::KW>(kbase + off + r16 * slot_b + C::DQ * g * C::EB, t.k[hb]);
+        else
+#pragma unroll
+          for (int i = 0; i < C::KW; ++i) t.k[hb][i] = 0;
+      }
+#pragma unroll
+      for (int jj = 0; jj < 4; ++jj) {
+        const int key = kb0 + 4 * g + jj;
+        if (live && key >= kl && key < k1)
+          load_dw<C::VW>(vbase + off + (4 * g + jj) * slot_b + C::E * r16 * C::EB,
+                         t.v[4 * hb + jj]);
+        else
+#pragma unroll
+          for (int i = 0; i < C::VW; ++i) t.v[4 * hb + jj][i] = 0;
+      }
+    } else {
+      {
+        const int key = kb0 + r16;
+        if (key >= kl && key < k1) {
+          const uint32_t bi = fastdiv((uint32_t)key, p.bs_div);
+          const int slot = key - (int)bi * p.block_size;
+          const int64_t off = (int64_t)bt_row[bi] * blk_b + (int64_t)slot * slot_b;
+          load_dw<C::KW>(kbase + off + C::DQ * g * C::EB, t.k[hb]);
+        } else {
+#pragma unroll
+          for (int i = 0; i < C::KW; ++i) t.k[hb][i] = 0;
+        }
+      }
+#pragma unroll
+      for (int jj = 0; jj < 4; ++jj) {
+        const int key = kb0 + 4 * g + jj;
+        if (key >= kl && key < k1) {
+          const uint32_t bi = fastdiv((uint32_t)key, p.bs_div);
+          const int slot = key - (int)bi * p.block_size;
+          const int64_t off = (int64_t)bt_row[bi] * blk_b + (int64_t)slot * slot_b;
+          load_dw<C::VW>(vbase + off + C::E * r16 * C::EB, t.v[4 * hb + jj]);
+        } else {
+#pragma unroll
+          for (int i = 0; i < C::VW; ++i) t.v[4 * hb + jj][i] = 0;
+        }
+      }
+    }
+  }
+}
+
+// A operand of the c-th QK MFMA for key half hb: 8 head-dim values of the
+// lane's K row (head-dim index D/4 * g + 8 c + j, matching the Q operand).
+template <int QT, bool FP8, int D>
+__device__ __forceinline__ u32x4 k_operand(const Tile<QT, FP8, D>& t, int hb, int c) {
+  if constexpr (FP8) {
+    u32x2 raw = {t.k[hb][2 * c], t.k[hb][2 * c + 1]};
+    return fp8x8_to<QT>(raw);
+  } else {
+    u32x4 r = {t.k[hb][4 * c], t.k[hb][4 * c + 1], t.k[hb][4 * c + 2], t.k[hb][4 * c + 3]};
+    return r;
+  }
+}
+
+// A operand of the c-th PV MFMA (O^T = V^T P^T).  Lane l supplies
+// V[key_j][E*(l%16) + c] for its eight keys j (j < 4: 4g + j, else
+// 16 + 4g + j - 4), two keys per dword.
+template <int QT, bool FP8, int D>
+__device__ __forceinline__ u32x4 v_operand(const Tile<QT, FP8, D>& t, int c) {
+  u32x4 op;
+  if constexpr (!FP8) {
+    const uint32_t sel = (c & 1) ? 0x07060302u : 0x05040100u;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) op[q] = perm_b32(t.v[2 * q + 1][c >> 1], t.v[2 * q][c >> 1], sel);
+  } else {
+    // Gather byte c of keys 2q and 2q+1 into the low half, then convert the pair.
+    const uint32_t bc = c & 3;
+    const uint32_t sel = bc | ((bc + 4) << 8) | 0x0c0c0000u;
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+      op[q] = fp8x2_to<QT>(perm_b32(t.v[2 * q + 1][c >> 2], t.v[2 * q][c >> 2], sel), false);
+  }
+  return op;
+}
+
+template <int QT, bool FP8, int D, bool SPLIT, bool PAGE16>
+__global__ __launch_bounds__(256, 2) void small_kernel(Params p) {
+  using C = SmallCfg<QT, FP8, D>;
+  constexpr int E = C::E;
+  constexpr int QC = C::QC;
+  constexpr int DQ = C::DQ;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6;
+  const int g = lane >> 4, r16 = lane & 15;
+  const int qb = blockIdx.x, kvh = blockIdx.y, part = blockIdx.z;
+
+  const int s = find_seq(p.cu_seqlens_q, p.num_seqs, qb, p.block_q);
+  const int q_start = p.cu_seqlens_q[s], q_end = p.cu_seqlens_q[s + 1];
+  const int tok0 = q_start + (qb - (q_start / p.block_q + s)) * p.block_q;
+  if (tok0 >= q_end) return;
+  const int ntok = min(p.block_q, q_end - tok0);
+  const int kv_len = p.seq_lens[s];
+  const int ctx = kv_len - (q_end - q_start);
+  const int p0 = ctx + (tok0 - q_start);  // position of the block's first query
+  const int hi = p0 + ntok;               // keys >= hi are invisible to every row
+  const int lo = p.window > 0 ? max(0, p0 - p.window + 1) : 0;
+  const int lo_a = lo & ~31;
+  const int plen = ((hi - lo_a + p.n_part - 1) / p.n_part + 31) & ~31;
+  const int k0 = lo_a + part * plen;
+  const int k1 = min(k0 + plen, hi);
+  const int kl = max(k0, lo);
+  const int G = p.group;
+  const int R = p.total_q * p.num_q_heads;
+
+  __shared__ float sm_m[kSmallWaves][16];
+  __shared__ float sm_l[kSmallWaves][16];
+  __shared__ float sm_o[kSmallWaves][16][D + 4];
+
+  if (k0 >= k1) {
+    // Empty partition: l = 0 tells the reduce to skip it.
+    if constexpr (SPLIT) {
+      if (tid < 16) {
+        const int rt = tid / G, rh = tid - (tid / G) * G;
+        if (tid < p.block_q * G && rt < ntok) {
+          const int64_t row = (int64_t)(tok0 + rt) * p.num_q_heads + kvh * G + rh;
+          p.ws_l[(int64_t)part * R + row] = 0.0f;
+          p.ws_m[(int64_t)part * R + row] = -INFINITY;
+        }
+      }
+    }
+    return;
+  }
+
+  // This lane's query row.
+  const int rt = r16 / G, rh = r16 - rt * G;
+  const bool row_ok = (r16 < p.block_q * G) && (rt < ntok);
+  const int h = kvh * G + rh;
+  const int pos = p0 + rt;
+  const int row_lo = p.window > 0 ? max(kl, pos - p.window + 1) : kl;
+  const int row_hi = min(k1, pos + 1);
+  const float slope2 = (p.alibi != nullptr && row_ok) ? p.alibi[h] * kLog2e : 0.0f;
+
+  // Q as the B operand of S^T = K Q^T: lane holds head-dim values [DQ*g, DQ*g + DQ).
+  u32x4 qop[QC];
+  if (row_ok) {
+    const char* qp = reinterpret_cast<const char*>(p.q) +
+                     ((int64_t)(tok0 + rt) * p.q_stride_tok + (int64_t)h * p.q_stride_head +
+                      DQ * g) * 2;
+#pragma unroll
+    for (int c = 0; c < QC; ++c) qop[c] = *reinterpret_cast<const u32x4*>(qp + 16 * c);
+  } else {
+#pragma unroll
+    for (int c = 0; c < QC; ++c) qop[c] = u32x4{0, 0, 0, 0};
+  }
+
+  const int32_t* bt_row = p.block_table + (int64_t)s * p.max_blocks_per_seq;
+  const char* kbase = reinterpret_cast<const char*>(p.k) + kvh * p.kv_stride_head * C::EB;
+  const char* vbase = reinterpret_cast<const char*>(p.v) + kvh * p.kv_stride_head * C::EB;
+
+  f32x4 oacc[E];
+#pragma unroll
+  for (int c = 0; c < E; ++c) oacc[c] = f32x4{0.f, 0.f, 0.f, 0.f};
+  float m_run = -INFINITY, l_run = 0.0f;
+
+  auto compute = [&](const Tile<QT, FP8, D>& t, int kt) {
+    f32x4 sacc[2];
+#pragma unroll
+    for (int hb = 0; hb < 2; ++hb) {
+      sacc[hb] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int c = 0; c < QC; ++c) sacc[hb] = mfma16<QT>(k_operand(t, hb, c), qop[c], sacc[hb]);
+    }
+    float x[8];
+    float mt = -INFINITY;
+#pragma unroll
+    for (int hb = 0; hb < 2; ++hb) {
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int key = kt + 16 * hb + 4 * g + r;
+        const float raw = sacc[hb][r];
+        float v = p.softcap_on ? p.cap_out2 * tanh_fast(raw * p.cap_in) : raw * p.qk_scale2;
+        v += slope2 * (float)(key - ctx);
+        const bool vis = key >= row_lo && key < row_hi;
+        x[4 * hb + r] = vis ? v : -INFINITY;
+        mt = fmaxf(mt, x[4 * hb + r]);
+      }
+    }
+    mt = wave_max_xor(mt, 16);
+    mt = wave_max_xor(mt, 32);
+    const float m_new = fmaxf(m_run, mt);
+    const float m_use = (m_new == -INFINITY) ? 0.0f : m_new;
+    const float alpha = fast_exp2(m_run - m_use);
+    m_run = m_new;
+    u32x4 pb;
+    float psum = 0.0f;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const uint32_t pk = pack2<QT>(fast_exp2(x[2 * q] - m_use), fast_exp2(x[2 * q + 1] - m_use));
+      pb[q] = pk;
+      psum += lo16<QT>(pk) + hi16<QT>(pk);
+    }
+    l_run = l_run * alpha + psum;
+#pragma unroll
+    for (int c = 0; c < E; ++c) oacc[c] *= alpha;
+#pragma unroll
+    for (int c = 0; c < E; ++c) oacc[c] = mfma16<QT>(v_operand(t, c), pb, oacc[c]);
+  };
+
+  // Two-stage register pipeline: the next tile's loads are in flight while
+  // the current tile is computed.
+  int kt = k0 + kSmallTile * wave;
+  constexpr int kStride = kSmallTile * kSmallWaves;
+  if constexpr (D > 128) {
+    // A 256-wide tile is 128 registers per lane: no second stage.
+    for (; kt < k1; kt += kStride) {
+      Tile<QT, FP8, D> t1;
+      load_tile<QT, FP8, D, PAGE16>(t1, p, bt_row, kbase, vbase, kt, kl, k1, g, r16);
+      compute(t1, kt);
+    }
+  } else {
+  Tile<QT, FP8, D> ta, tb;
+  if (kt < k1) load_tile<QT, FP8, D, PAGE16>(ta, p, bt_row, kbase, vbase, kt, kl, k1, g, r16);
+  while (kt < k1) {
+    if (kt + kStride < k1)
+      load_tile<QT, FP8, D, PAGE16>(tb, p, bt_row, kbase, vbase, kt + kStride, kl, k1, g, r16);
+    compute(ta, kt);
+    kt += kStride;
+    if (kt >= k1) break;
+    if (kt + kStride < k1)
+      load_tile<QT, FP8, D, PAGE16>(ta, p, bt_row, kbase, vbase, kt + kStride, kl, k1, g, r16);
+    compute(tb, kt);
+    kt += kStride;
+  }
+  }
+
+  // Merge the four waves' states through LDS.
+  float l_row = wave_sum_xor(l_run, 16);
+  l_row = wave_sum_xor(l_row, 32);
+  if (g == 0) {
+    sm_m[wave][r16] = m_run;
+    sm_l[wave][r16] = l_row;
+  }
+  // O^T accumulator: register (c, r) holds O[row l%16][D/4*g + E*r + c].
+#pragma unroll
+  for (int c = 0; c < E; ++c)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) sm_o[wave][r16][DQ * g + E * r + c] = oacc[c][r];
+  __syncthreads();
+
+  const int row = tid >> 4, chunk = tid & 15;
+  const int mrt = row / G, mrh = row - (row / G) * G;
+  if (!(row < p.block_q * G && mrt < ntok)) return;
+  const int tok = tok0 + mrt, hh = kvh * G + mrh;
+  float mw[kSmallWaves];
+  float M = -INFINITY;
+#pragma unroll
+  for (int w = 0; w < kSmallWaves; ++w) {
+    mw[w] = sm_m[w][row];
+    M = fmaxf(M, mw[w]);
+  }
+  const float sink2 = (!SPLIT && p.sinks != nullptr) ? p.sinks[hh] * kLog2e : -INFINITY;
+  const float Mt = fmaxf(M, sink2);
+  const float Ms = (Mt == -INFINITY) ? 0.0f : Mt;
+  float L = 0.0f;
+  float f[kSmallWaves];
+#pragma unroll
+  for (int w = 0; w < kSmallWaves; ++w) {
+    f[w] = fast_exp2(mw[w] - Ms);
+    L += f[w] * sm_l[w][row];
+  }
+  const bool any_key = L > 0.0f;
+  float o[E];
+#pragma unroll
+  for (int e = 0; e < E; ++e) {
+    float a = 0.0f;
+#pragma unroll
+    for (int w = 0; w < kSmallWaves; ++w) a += f[w] * sm_o[w][row][E * chunk + e];
+    o[e] = a;
+  }
+  const int64_t rrow = (int64_t)tok * p.num_q_heads + hh;
+  if constexpr (SPLIT) {
+    if (chunk == 0) {
+      p.ws_m[(int64_t)part * R + rrow] = M;
+      p.ws_l[(int64_t)part * R + rrow] = L;
+    }
+    float* dst = p.ws_acc + ((int64_t)part * R + rrow) * D + E * chunk;
+#pragma unroll
+    for (int e = 0; e < E; e += 4)
+      *reinterpret_cast<f32x4*>(dst + e) = f32x4{o[e], o[e + 1], o[e + 2], o[e + 3]};
+  } else {
+    if (sink2 != -INFINITY) L += fast_exp2(sink2 - Ms);
+    const float inv = any_key ? p.v_scale / L : 0.0f;
+    uint32_t packed[E / 2];
+#pragma unroll
+    for (int e = 0; e < E; e += 2) packed[e / 2] = pack2<QT>(o[e] * inv, o[e + 1] * inv);
+    char* dst = reinterpret_cast<char*>(p.out) +
+                ((int64_t)tok * p.o_stride_tok + (int64_t)hh * p.o_stride_head + E * chunk) * 2;
+    if constexpr (E == 8) {
+      *reinterpret_cast<u32x4*>(dst) = u32x4{packed[0], packed[1], packed[2], packed[3]};
+    } else if constexpr (E == 16) {
+      *reinterpret_cast<u32x4*>(dst) = u32x4{packed[0], packed[1], packed[2], packed[3]};
+      *reinterpret_cast<u32x4*>(dst + 16) = u32x4{packed[4], packed[5], packed[6], packed[7]};
+    } else {
+      *reinterpret_cast<u32x2*>(dst) = u32x2{packed[0], packed[1]};
+    }
+    if (p.lse != nullptr && chunk == 0)
+      p.lse[rrow] = (L > 0.0f) ? (Ms + fast_log2(L)) * kLn2 : -INFINITY;
+  }
+}
+
+template <int QT, bool FP8, int D>
+hipError_t launch_small_t(const Params& p, bool split, dim3 grid, hipStream_t stream) {
+  const bool page16 = (p.block_size % 16) == 0;
+  if (split) {
+    if (page16)
+      hipLaunchKernelGGL((small_kernel<QT, FP8, D, true, true>), grid, dim3(256), 0, stream, p);
+    else
+      hipLaunchKernelGGL((small_kernel<QT, FP8, D, true, false>), grid, dim3(256), 0, stream, p);
+  } else {
+    if (page16)
+      hipLaunchKernelGGL((small_kernel<QT, FP8, D, false, true>), grid, dim3(256), 0, stream, p);
+    else
+      hipLaunchKernelGGL((small_kernel<QT, FP8, D, false, false>), grid, dim3(256), 0, stream, p);
+  }
+  return hipGetLastError();
+}
+
+template <int QT, bool FP8>
+hipError_t launch_small_d(const Params& p, int head_dim, bool split, dim3 grid,
+                          hipStream_t stream) {
+  switch (head_dim) {
+    case 64: return launch_small_t<QT, FP8, 64>(p, split, grid, stream);
+    case 128: return launch_small_t<QT, FP8, 128>(p, split, grid, stream);
+    case 256: return launch_small_t<QT, FP8, 256>(p, split, grid, stream);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+}  // namespace
+
+hipError_t launch_small(const Params& p, int q_dtype, int kv_fp8, int head_dim, bool split,
+                        dim3 grid, hipStream_t stream) {
+  if (q_dtype == UA_F16)
+    return kv_fp8 ? launch_small_d<UA_F16, true>(p, head_dim, split, grid, stream)
+                  : launch_small_d<UA_F16, false>(p, head_dim, split, grid, stream);
+  return kv_fp8 ? launch_small_d<UA_BF16, true>(p, head_dim, split, grid, stream)
+                : launch_small_d<UA_BF16, false>(p, head_dim, split, grid, stream);
+}
+
+}  // namespace ua

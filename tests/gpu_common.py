@@ -1,0 +1,114 @@
+"""Helpers shared by the GPU parity tests and smoke(): upload a seeded case,
+run it through the C ABI, compare with the oracle.
+
+Tolerances (max-abs against the float64 oracle; fp8 KV against the oracle on
+the dequantised cache): fp16 2e-3, bf16 1e-2, fp8 KV 2e-2.  Each element may
+additionally differ by half a unit in the last place of the output type at the
+oracle's value: that is the error of rounding the exact result once to the
+output type, which no kernel can avoid (bf16 half-ULP is 7.8e-3 on [2, 4)).
+"""
+
+import math
+
+import numpy as np
+import torch
+
+TOL = {"f16": 2e-3, "bf16": 1e-2, "e4m3fn": 2e-2}
+_MANT = {"f16": 10, "bf16": 7}
+
+
+def tolerance(case):
+    return TOL["e4m3fn"] if case["kv_dtype"] == "e4m3fn" else TOL[case["q_dtype"]]
+
+
+def half_ulp(ref, o_dtype):
+    a = np.abs(ref)
+    e = np.floor(np.log2(np.where(a > 0, a, 1.0)))
+    e = np.maximum(e, -14 if o_dtype == "f16" else -126)
+    return np.where(a > 0, 2.0 ** (e - _MANT[o_dtype] - 1), 0.0)
+
+
+def _torch_bits(arr, dtype, device):
+    t = torch.from_numpy(np.ascontiguousarray(arr))
+    if dtype == "f16":
+        return t.view(torch.int16).view(torch.float16).to(device)
+    if dtype == "bf16":
+        return t.view(torch.int16).view(torch.bfloat16).to(device)
+    return t.view(torch.uint8).view(torch.float8_e4m3fn).to(device)
+
+
+def to_device(case, device="cuda"):
+    d = dict(
+        q=_torch_bits(case["q"], case["q_dtype"], device),
+        k_cache=_torch_bits(case["k_cache"], case["kv_dtype"], device),
+        v_cache=_torch_bits(case["v_cache"], case["kv_dtype"], device),
+        block_table=torch.from_numpy(case["block_table"]).to(device),
+        cu_seqlens_q=torch.from_numpy(case["cu_seqlens_q"]).to(device),
+        seq_lens=torch.from_numpy(case["seq_lens"]).to(device),
+        alibi_slopes=(None if case["alibi_slopes"] is None
+                      else torch.from_numpy(np.asarray(case["alibi_slopes"], np.float32)).to(device)),
+        sinks=(None if case["sinks"] is None
+               else torch.from_numpy(np.asarray(case["sinks"], np.float32)).to(device)),
+    )
+    return d
+
+
+def run(case, dev=None, path="auto", n_part=0, lse=False, poison_out=True, ws=None,
+        out=None):
+    """Run one case on the GPU through the C ABI; returns (out fp64 numpy, lse, plan)."""
+    import paged_varlen_attention_ua_amd.attention as A
+    dev = dev or to_device(case)
+    q = dev["q"]
+    if out is None:
+        out = torch.empty_like(q)
+        if poison_out:
+            out.fill_(float("nan"))
+    lse_t = None
+    if lse:
+        lse_t = torch.full(q.shape[:2], float("nan"), dtype=torch.float32, device=q.device)
+    o, plan = A.forward(q, dev["k_cache"], dev["v_cache"], dev["block_table"],
+                        dev["cu_seqlens_q"], dev["seq_lens"],
+                        max_seqlen_q=case["max_seqlen_q"], max_seqlen_k=case["max_seqlen_k"],
+                        scale=case["scale"], softcap=case["softcap"], window=case["window"],
+                        k_scale=case["k_scale"], v_scale=case["v_scale"],
+                        alibi_slopes=dev["alibi_slopes"], sinks=dev["sinks"], out=out,
+                        lse=lse_t, path=path, n_part=n_part, ws=ws)
+    torch.cuda.synchronize()
+    res = o.float().cpu().numpy().astype(np.float64)
+    l = lse_t.cpu().numpy().astype(np.float64) if lse_t is not None else None
+    return res, l, plan
+
+
+def compare(case, got, ref, rows=None, label=""):
+    """Assert |got - ref| <= tol + half_ulp(ref) elementwise; return max-abs error."""
+    if rows is not None:
+        got = got[rows]
+    tol = tolerance(case)
+    err = np.abs(got - ref)
+    allowed = tol + half_ulp(ref, case["o_dtype"])
+    bad = ~(err <= allowed)  # NaN counts as bad
+    if bad.any():
+        idx = np.argwhere(bad)[:5]
+        raise AssertionError(
+            f"{label}: {int(bad.sum())} elements outside tolerance {tol}; max err "
+            f"{np.nanmax(err) if np.isfinite(err).any() else float('nan')}; first "
+            f"{[(tuple(i), float(got[tuple(i)]), float(ref[tuple(i)])) for i in idx]}")
+    return float(err.max()) if err.size else 0.0
+
+
+def sample_rows(total_q, n, seed):
+    """First, last and random query rows (sorted, unique) for full-size sampled parity."""
+    rng = np.random.default_rng(seed)
+    k = min(total_q, n)
+    base = set(range(min(8, total_q))) | set(range(max(0, total_q - 8), total_q))
+    base |= set(rng.choice(total_q, size=k, replace=False).tolist())
+    return np.array(sorted(base), dtype=np.int64)
+
+
+def check_lse(got, ref, atol=2e-3, label=""):
+    """LSE (natural log, fp32 on the GPU): same -inf pattern, finite values within atol."""
+    fin = np.isfinite(ref)
+    assert np.array_equal(np.isneginf(got), ~fin), f"{label}: -inf pattern of lse differs"
+    err = np.abs(got[fin] - ref[fin]).max() if fin.any() else 0.0
+    assert err <= atol, f"{label}: lse max err {err}"
+    return float(err)

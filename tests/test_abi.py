@@ -1,0 +1,162 @@
+"""CPU tests of the C-ABI library: exported symbols and the pure-host planner.
+
+No kernel is launched: ua_plan is a host function, and the forward entry
+points are only called on inputs they must reject before any launch.
+"""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+import paged_varlen_attention_ua_amd as U
+from paged_varlen_attention_ua_amd import binding as B
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _declared_functions():
+    src = open(os.path.join(ROOT, "include", "ua.h")).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?[a-z_0-9]+\s*\*?\s*(ua_[a-z_0-9]+)\s*\(",
+                                 src, flags=re.M)))
+
+
+def test_header_declares_the_four_entry_points():
+    names = _declared_functions()
+    for fn in ("ua_plan", "ua_forward_2d", "ua_forward_splitkv", "ua_reduce"):
+        assert fn in names
+
+
+def test_library_exports_every_declared_symbol():
+    lib = ctypes.CDLL(B.LIB_PATH)
+    for fn in _declared_functions():
+        assert hasattr(lib, fn), fn
+    assert U.ua_abi_version() == 1
+
+
+def test_struct_sizes_match_header_layout():
+    # ua_problem: 6 int32, int64, 3 int32, 3 int32, 2 float, int32, 2 float, 2 int32, pad, 7 int64
+    assert ctypes.sizeof(B.UaProblem) == 144
+    assert ctypes.sizeof(B.UaPlan) == 48
+    assert ctypes.sizeof(B.UaArgs) == 80
+
+
+def problem(**kw):
+    p = B.UaProblem()
+    d = dict(num_seqs=8, total_q=8, num_q_heads=32, num_kv_heads=8, head_dim=128,
+             block_size=16, num_blocks=1000, max_blocks_per_seq=500, max_seqlen_q=1,
+             max_seqlen_k=6900, q_dtype=B.UA_BF16, kv_dtype=B.UA_BF16, o_dtype=B.UA_BF16,
+             scale=0.088, softcap=0.0, window=4096, k_scale=1.0, v_scale=1.0, has_alibi=0,
+             has_sinks=0)
+    d.update(kw)
+    D, H, Hk = d["head_dim"], d["num_q_heads"], d["num_kv_heads"]
+    d.setdefault("q_stride_tok", H * D)
+    d.setdefault("q_stride_head", D)
+    d.setdefault("o_stride_tok", H * D)
+    d.setdefault("o_stride_head", D)
+    d.setdefault("kv_stride_block", d["block_size"] * Hk * D)
+    d.setdefault("kv_stride_slot", Hk * D)
+    d.setdefault("kv_stride_head", D)
+    for k, v in d.items():
+        setattr(p, k, v)
+    return p
+
+
+def status_of(p, force_path=0, n_part=0):
+    plan = B.UaPlan()
+    return B.lib().ua_plan(ctypes.byref(p), 256, force_path, n_part, ctypes.byref(plan)), plan
+
+
+def test_long_decode_splits_to_fill_the_device():
+    st, plan = status_of(problem())
+    assert st == 0 and plan.path == B.UA_PATH_SPLITKV
+    assert plan.n_part == 16  # 8 seqs x 8 kv heads = 64 groups, 4096-key window
+    assert plan.grid_y == 8 and plan.grid_z == 16
+    R = 8 * 32
+    assert plan.workspace_bytes == ((2 * 16 * R * 4 + 255) & ~255) + 16 * R * 128 * 4
+
+
+def test_short_context_full_grid_stays_one_pass():
+    st, plan = status_of(problem(num_seqs=32, total_q=32, max_seqlen_k=630))
+    assert st == 0 and plan.path == B.UA_PATH_2D and plan.n_part == 1
+    assert plan.workspace_bytes == 0
+
+
+def test_forced_paths():
+    st, plan = status_of(problem(), force_path=B.UA_PATH_2D)
+    assert st == 0 and plan.path == B.UA_PATH_2D and plan.n_part == 1
+    st, plan = status_of(problem(num_seqs=32, total_q=32, max_seqlen_k=630),
+                         force_path=B.UA_PATH_SPLITKV, n_part=7)
+    assert st == 0 and plan.path == B.UA_PATH_SPLITKV and plan.n_part == 7
+    st, _ = status_of(problem(), force_path=B.UA_PATH_2D, n_part=4)
+    assert st == -1
+
+
+def test_grid_covers_every_query_block():
+    # slots = total_q / block_q + num_seqs >= sum ceil(q_len / block_q)
+    st, plan = status_of(problem(num_seqs=5, total_q=327, max_seqlen_q=129, max_seqlen_k=1328,
+                                 num_q_heads=16, num_kv_heads=2, window=0))
+    assert st == 0
+    bq = plan.block_q
+    lens = [1, 5, 129, 64, 128]
+    assert sum(-(-q // bq) for q in lens) <= plan.grid_x == 327 // bq + 5
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(num_q_heads=30, num_kv_heads=8), -1),
+    (dict(head_dim=96), -2),
+    (dict(block_size=0), -1),
+    (dict(max_seqlen_q=7000), -1),
+    (dict(max_blocks_per_seq=10), -1),
+    (dict(q_dtype=B.UA_FP8_E4M3FN), -2),
+    (dict(kv_dtype=B.UA_F16), -2),
+    (dict(o_dtype=B.UA_F16), -2),
+    (dict(scale=float("nan")), -1),
+    (dict(softcap=float("inf")), -1),
+    (dict(kv_dtype=B.UA_FP8_E4M3FN, k_scale=0.0), -1),
+    (dict(kv_stride_slot=1028), -2),
+    (dict(q_stride_head=0), -1),
+    (dict(total_q=9), -1),
+])
+def test_invalid_problems_are_rejected(kw, code):
+    st, _ = status_of(problem(**kw))
+    assert st == code
+
+
+def test_forward_rejects_mismatched_plan_and_missing_workspace():
+    p = problem()
+    st, plan = status_of(p)
+    args = B.UaArgs()
+    # plan made for another problem
+    p2 = problem(window=100)
+    assert B.lib().ua_forward_2d(ctypes.byref(p2), ctypes.byref(plan), ctypes.byref(args),
+                                 None) == -5
+    # split plan passed to the 2D entry point
+    assert B.lib().ua_forward_2d(ctypes.byref(p), ctypes.byref(plan), ctypes.byref(args),
+                                 None) == -5
+    # missing device pointers
+    assert B.lib().ua_forward_splitkv(ctypes.byref(p), ctypes.byref(plan), ctypes.byref(args),
+                                      None, 0, None) == -1
+    # workspace too small (pointers set to fake aligned non-null values; nothing launches)
+    for f in ("q", "k_cache", "v_cache", "block_table", "cu_seqlens_q", "seq_lens", "out"):
+        setattr(args, f, 1 << 20)
+    assert B.lib().ua_forward_splitkv(ctypes.byref(p), ctypes.byref(plan), ctypes.byref(args),
+                                      ctypes.c_void_p(1 << 21), 16, None) == -3
+    assert B.lib().ua_reduce(ctypes.byref(p), ctypes.byref(plan), ctypes.byref(args),
+                             None, 0, None) == -3
+
+
+def test_empty_batch_is_a_no_op():
+    p = problem(num_seqs=0, total_q=0, max_seqlen_q=0, max_seqlen_k=0)
+    st, plan = status_of(p)
+    assert st == 0 and plan.grid_x == 0
+    args = B.UaArgs()
+    assert B.lib().ua_forward(ctypes.byref(p), ctypes.byref(plan), ctypes.byref(args), None, 0,
+                              None) == 0
+
+
+def test_status_strings():
+    assert B.lib().ua_status_string(0) == b"ok"
+    assert B.lib().ua_status_string(-3).startswith(b"workspace")

@@ -1,0 +1,278 @@
+"""GPU parity: the HIP path (through the C ABI) against the float64 oracle.
+
+Every case is seeded; unused cache blocks, slots past kv_len, the block-table
+padding block, the output buffer and the split-KV workspace are NaN-poisoned,
+so any read of them or any unwritten output shows up as a failure.
+"""
+
+import ctypes
+import functools
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from synth import WORKLOADS, make_case
+from tests.gpu_common import (check_lse, compare, run, sample_rows, to_device, tolerance)
+
+pytestmark = pytest.mark.gpu
+
+PATHS = [("auto", 0), ("2d", 0), ("splitkv", 1), ("splitkv", 4), ("splitkv", 7), ("splitkv", 16)]
+
+
+@functools.lru_cache(maxsize=None)
+def _workload(name):
+    case = make_case(**WORKLOADS[name])
+    ref, lse = oracle.attention(**case)
+    return case, ref, lse
+
+
+@functools.lru_cache(maxsize=None)
+def _dev(name):
+    return to_device(_workload(name)[0])
+
+
+DECODE_AND_MIXED = [
+    "decode_fp16_d128_16q2kv",
+    "mixed_fp16_d128_16q2kv",
+    "mixed_fp16_d128_16q2kv_alibi",
+    "long_decode_bf16_d128_32q8kv_w4096",
+    "long_decode_bf16_d128_32q8kv_w4096_softcap_sinks",
+    "fp8kv_decode_b32_ctx590",
+    "fp8kv_decode_b8_ctx6700_w4096",
+]
+
+
+@pytest.mark.parametrize("path,n_part", PATHS, ids=[f"{p}{n}" for p, n in PATHS])
+@pytest.mark.parametrize("name", DECODE_AND_MIXED)
+def test_workload_full_size(name, path, n_part):
+    case, ref, ref_lse = _workload(name)
+    print(f"[case] {name} path={path} n_part={n_part}", flush=True)
+    got, lse, plan = run(case, _dev(name), path=path, n_part=n_part, lse=True)
+    err = compare(case, got, ref, label=f"{name}/{path}{n_part}")
+    check_lse(lse, ref_lse, label=name)
+    print(f"[ok] {name} path={plan.path} n_part={plan.n_part} max_abs={err:.3e}", flush=True)
+
+
+PREFILL = ["prefill_chunk1k_prefix8k_bf16", "prefill_chunk2k_prefix16k_bf16",
+           "prefill_4x1k_bf16", "prefill_8k_d256_24q4kv_bs784_bf16"]
+
+
+@pytest.mark.parametrize("path,n_part", [("auto", 0), ("splitkv", 3)])
+@pytest.mark.parametrize("name", PREFILL)
+def test_prefill_full_size_sampled_rows(name, path, n_part):
+    case = make_case(**WORKLOADS[name])
+    total_q = case["q"].shape[0]
+    rows = sample_rows(total_q, 48, seed=7)
+    ref, ref_lse = oracle.attention(**case, rows=rows)
+    print(f"[case] {name} path={path} rows={len(rows)}", flush=True)
+    got, lse, plan = run(case, path=path, n_part=n_part, lse=True)
+    assert np.isfinite(got).all(), "unwritten or NaN output rows"
+    err = compare(case, got, ref, rows=rows, label=name)
+    check_lse(lse[rows], ref_lse, label=name)
+    print(f"[ok] {name} path={plan.path} max_abs={err:.3e}", flush=True)
+
+
+# ----------------------------------------------------------------------------- edge cases
+
+def _check(case, path="auto", n_part=0, lse=True, label=""):
+    ref, ref_lse = oracle.attention(**case)
+    got, l, plan = run(case, path=path, n_part=n_part, lse=lse)
+    err = compare(case, got, ref, label=label)
+    if lse:
+        check_lse(l, ref_lse, label=label)
+    return err, plan
+
+
+BASE = dict(head_dim=128, num_q_heads=16, num_kv_heads=2, block_size=16, q_dtype="bf16")
+MIXED_SEQS = [(1, 300), (17, 90), (0, 12), (40, 40), (1, 1), (33, 700)]
+
+
+@pytest.mark.parametrize("path,n_part", [("2d", 0), ("splitkv", 5)])
+def test_empty_sequences(path, n_part):
+    case = make_case(seqs=[(0, 0), (3, 10), (0, 7), (1, 1), (0, 0), (2, 40)], seed=11, **BASE)
+    _check(case, path, n_part, label="empty")
+
+
+@pytest.mark.parametrize("window", [1, 17, 100])
+@pytest.mark.parametrize("path,n_part", [("2d", 0), ("splitkv", 3)])
+def test_windows(window, path, n_part):
+    case = make_case(seqs=MIXED_SEQS, window=window, seed=12 + window, **BASE)
+    _check(case, path, n_part, label=f"w{window}")
+
+
+@pytest.mark.parametrize("bs", [1, 3, 13, 32, 784])
+@pytest.mark.parametrize("path,n_part", [("2d", 0), ("splitkv", 4)])
+def test_block_sizes(bs, path, n_part):
+    case = make_case(seqs=MIXED_SEQS, seed=20 + bs, **dict(BASE, block_size=bs))
+    _check(case, path, n_part, label=f"bs{bs}")
+
+
+@pytest.mark.parametrize("D", [64, 128, 256])
+@pytest.mark.parametrize("dt,kvd", [("f16", "f16"), ("bf16", "bf16"), ("bf16", "e4m3fn"),
+                                     ("f16", "e4m3fn")])
+def test_head_dims_and_dtypes(D, dt, kvd):
+    case = make_case(seqs=MIXED_SEQS, seed=30 + D, **dict(BASE, head_dim=D, q_dtype=dt,
+                                                           kv_dtype=kvd))
+    _check(case, "auto", 0, label=f"D{D}-{dt}-{kvd}")
+    _check(case, "splitkv", 3, label=f"D{D}-{dt}-{kvd}-split")
+
+
+@pytest.mark.parametrize("Hq,Hkv", [(4, 4), (6, 2), (24, 4), (32, 2), (8, 1)])
+def test_group_sizes(Hq, Hkv):
+    case = make_case(seqs=MIXED_SEQS, seed=40 + Hq, **dict(BASE, num_q_heads=Hq,
+                                                            num_kv_heads=Hkv))
+    _check(case, "2d", 0, label=f"G{Hq // Hkv}")
+    _check(case, "splitkv", 4, label=f"G{Hq // Hkv}-split")
+
+
+@pytest.mark.parametrize("path,n_part", [("2d", 0), ("splitkv", 3)])
+def test_features_visible_at_tolerance(path, n_part):
+    """Softcap 3, sinks on short sequences and ALiBi: each moves outputs >> tol."""
+    seqs = [(1, 4), (3, 6), (2, 300), (5, 60)]
+    for kw in [dict(softcap=3.0), dict(sinks=True), dict(alibi=True),
+               dict(softcap=3.0, sinks=True, window=9)]:
+        case = make_case(seqs=seqs, seed=50, **BASE, **kw)
+        _check(case, path, n_part, label=str(kw))
+
+
+def test_split_partition_counts_agree():
+    """Split-KV with any partition count equals one pass (within tolerance, pairwise)."""
+    case, ref, _ = _workload("long_decode_bf16_d128_32q8kv_w4096_softcap_sinks")
+    outs = []
+    for n in (1, 2, 4, 16, 31, 64):
+        got, _, _ = run(case, _dev("long_decode_bf16_d128_32q8kv_w4096_softcap_sinks"),
+                        path="splitkv", n_part=n)
+        compare(case, got, ref, label=f"n_part={n}")
+        outs.append(got)
+    one, _, _ = run(case, _dev("long_decode_bf16_d128_32q8kv_w4096_softcap_sinks"), path="2d")
+    for o in outs:
+        assert np.abs(o - one).max() <= tolerance(case)
+
+
+def test_nan_workspace_not_read():
+    case, ref, _ = _workload("fp8kv_decode_b8_ctx6700_w4096")
+    dev = _dev("fp8kv_decode_b8_ctx6700_w4096")
+    ws = torch.full((64 << 20,), 0xFF, dtype=torch.uint8, device="cuda")  # NaN bytes
+    got, _, _ = run(case, dev, path="splitkv", n_part=16, ws=ws)
+    compare(case, got, ref, label="nan-ws")
+
+
+def test_repeat_is_bit_identical():
+    case, _, _ = _workload("mixed_fp16_d128_16q2kv")
+    dev = _dev("mixed_fp16_d128_16q2kv")
+    a, _, _ = run(case, dev, path="splitkv", n_part=5)
+    b, _, _ = run(case, dev, path="splitkv", n_part=5)
+    assert np.array_equal(a, b)
+    c, _, _ = run(case, dev, path="2d")
+    d, _, _ = run(case, dev, path="2d")
+    assert np.array_equal(c, d)
+
+
+def test_two_streams_separate_workspaces():
+    import paged_varlen_attention_ua_amd.attention as A
+    c1, r1, _ = _workload("long_decode_bf16_d128_32q8kv_w4096")
+    c2, r2, _ = _workload("long_decode_bf16_d128_32q8kv_w4096_softcap_sinks")
+    d1, d2 = _dev("long_decode_bf16_d128_32q8kv_w4096"), \
+        _dev("long_decode_bf16_d128_32q8kv_w4096_softcap_sinks")
+    s1, s2 = torch.cuda.Stream(), torch.cuda.Stream()
+    outs = []
+    for c, d, s in ((c1, d1, s1), (c2, d2, s2)):
+        with torch.cuda.stream(s):
+            o = torch.full_like(d["q"], float("nan"))
+            A.forward(d["q"], d["k_cache"], d["v_cache"], d["block_table"], d["cu_seqlens_q"],
+                      d["seq_lens"], max_seqlen_q=c["max_seqlen_q"],
+                      max_seqlen_k=c["max_seqlen_k"], scale=c["scale"], softcap=c["softcap"],
+                      window=c["window"], sinks=d["sinks"], out=o, path="splitkv", n_part=16)
+            outs.append(o)
+    torch.cuda.synchronize()
+    compare(c1, outs[0].float().cpu().numpy().astype(np.float64), r1, label="stream1")
+    compare(c2, outs[1].float().cpu().numpy().astype(np.float64), r2, label="stream2")
+
+
+def test_reduce_alone_matches_oracle_merge():
+    """ua_reduce on random partition states equals the oracle's base-2 merge."""
+    import paged_varlen_attention_ua_amd as U
+    import paged_varlen_attention_ua_amd.attention as A
+    case = make_case(seqs=[(3, 50), (1, 20), (2, 9)], seed=60, sinks=True, **BASE)
+    dev = to_device(case)
+    P = 6
+    prob = A.make_problem(dev["q"], dev["k_cache"], dev["v_cache"], dev["block_table"],
+                          num_seqs=3, max_seqlen_q=3, max_seqlen_k=50, scale=case["scale"],
+                          sinks=dev["sinks"])
+    plan = U.ua_plan(prob, 256, U.UA_PATH_SPLITKV, P)
+    R = case["q"].shape[0] * 16
+    rng = np.random.default_rng(0)
+    m2 = rng.standard_normal((P, R)).astype(np.float32) * 4
+    l = rng.uniform(0.5, 30, (P, R)).astype(np.float32)
+    l[rng.random((P, R)) < 0.3] = 0.0
+    l[:, 5] = 0.0  # a row no partition saw
+    acc = rng.standard_normal((P, R, 128)).astype(np.float32) * 5
+    ws = torch.full((plan.workspace_bytes,), 0xFF, dtype=torch.uint8, device="cuda")
+    wf = ws.view(torch.float32)
+    wf[:P * R] = torch.from_numpy(m2.ravel()).cuda()
+    wf[P * R:2 * P * R] = torch.from_numpy(l.ravel()).cuda()
+    off = U.ua_workspace_acc_offset(prob, plan) // 4
+    acc_dev = torch.from_numpy(np.where(l[..., None] > 0, acc, np.nan).astype(np.float32).ravel())
+    wf[off:off + P * R * 128] = acc_dev.cuda()
+    out = torch.full_like(dev["q"], float("nan"))
+    lse = torch.full((R,), float("nan"), dtype=torch.float32, device="cuda")
+    args = A.make_args(dev["q"], dev["k_cache"], dev["v_cache"], dev["block_table"],
+                       dev["cu_seqlens_q"], dev["seq_lens"], out, lse=lse, sinks=dev["sinks"])
+    U.ua_reduce(prob, plan, args, ctypes.c_void_p(ws.data_ptr()), ws.numel(),
+                ctypes.c_void_p(torch.cuda.current_stream().cuda_stream))
+    torch.cuda.synchronize()
+    sinks = np.tile(case["sinks"].astype(np.float64), R // 16)
+    o_ref, lse_ref = oracle.merge_partials_base2(m2, l, acc, sinks)
+    got = out.float().cpu().numpy().reshape(R, 128).astype(np.float64)
+    compare(case, got, o_ref, label="reduce")
+    check_lse(lse.cpu().numpy().astype(np.float64), lse_ref, label="reduce-lse")
+
+
+def test_cache_offsets_beyond_2gib():
+    """Blocks placed past 2 GiB of cache: 64-bit block offsets (README 64-bit addressing)."""
+    case = make_case(seqs=[(1, 700), (5, 64), (1, 33)], seed=70, **dict(BASE, num_kv_heads=2))
+    ref, _ = oracle.attention(**case)
+    dev = to_device(case)
+    nb_small, bs, hk, d = case["k_cache"].shape
+    block_bytes = bs * hk * d * 2
+    shift = (3 << 30) // block_bytes  # 3 GiB into the cache
+    big_nb = shift + nb_small
+    kc = torch.full((big_nb, bs, hk, d), float("nan"), dtype=torch.bfloat16, device="cuda")
+    vc = torch.full_like(kc, float("nan"))
+    kc[shift:] = dev["k_cache"]
+    vc[shift:] = dev["v_cache"]
+    bt = dev["block_table"] + shift
+    big = dict(dev, k_cache=kc, v_cache=vc, block_table=bt)
+    for path, n in (("2d", 0), ("splitkv", 4)):
+        got, _, _ = run(case, big, path=path, n_part=n)
+        compare(case, got, ref, label=f"big-{path}")
+    del kc, vc
+    torch.cuda.empty_cache()
+
+
+def test_strided_query_output_and_cache():
+    """Q/O as views into wider buffers and a cache with padded head stride."""
+    import paged_varlen_attention_ua_amd.attention as A
+    case = make_case(seqs=MIXED_SEQS, seed=80, **BASE)
+    ref, _ = oracle.attention(**case)
+    dev = to_device(case)
+    T, H, D = dev["q"].shape
+    qbig = torch.zeros((T, H + 3, D + 8), dtype=dev["q"].dtype, device="cuda")
+    qbig[:, :H, :D] = dev["q"]
+    q = qbig[:, :H, :D]
+    nb, bs, hk, _ = dev["k_cache"].shape
+    kbig = torch.full((nb, bs, hk, D + 16), float("nan"), dtype=dev["q"].dtype, device="cuda")
+    vbig = torch.full_like(kbig, float("nan"))
+    kbig[..., :D] = dev["k_cache"]
+    vbig[..., :D] = dev["v_cache"]
+    obig = torch.full((T, H, D + 24), float("nan"), dtype=dev["q"].dtype, device="cuda")
+    o = obig[:, :, :D]
+    A.forward(q, kbig[..., :D], vbig[..., :D], dev["block_table"], dev["cu_seqlens_q"],
+              dev["seq_lens"], max_seqlen_q=case["max_seqlen_q"],
+              max_seqlen_k=case["max_seqlen_k"], scale=case["scale"], out=o, path="splitkv",
+              n_part=3)
+    torch.cuda.synchronize()
+    compare(case, o.float().cpu().numpy().astype(np.float64), ref, label="strided")
+    assert torch.isnan(obig[:, :, D:]).all(), "wrote outside the output view"
