@@ -1,0 +1,332 @@
+"""Benchmark of unified paged varlen attention on one MI355X.
+
+A step is one pass of the whole path over one batch: ua_plan on the host, the
+split-KV partition kernel and the reduce (or the one-pass kernel when the
+dispatcher picks it).  The headline workload is long-context decode, bf16,
+d128, 32 q / 8 kv heads, block size 16, batch 8 with kv_len uniform in
+[6500, 6900] and a 4096-key sliding window (the shape of AITER PR #3962's
+decode figure, section "Performance").  Its value is achieved GB/s of the
+algorithmic bytes (attended K and V rows + Q + O).
+
+Inputs are resident in HBM when timing starts and are rotated over R copies
+(addresses differ, so the 256 MB last-level cache cannot serve a repeat):
+R = max(2, ceil(1 GiB / bytes touched per step)).
+
+Also reported on the same line: the other decode workloads (GB/s), the
+chunked-prefill workloads (TFLOP/s of 4 * D * Hq * visible (q, k) pairs), the
+dominant kernel's roofline with HIP-event timing, and the CPU oracle's rate on
+a bounded sample (cpu_baseline).
+"""
+
+import argparse
+import ctypes
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+MFMA_PEAK_TFLOPS = {"f16": 2500.0, "bf16": 2500.0}
+HEADLINE = "long_decode_bf16_d128_32q8kv_w4096"
+METRIC = "decode KV GB/s (% of HBM peak) + prefill TFLOP/s (% MFMA peak), 1 GPU"
+EB = {"f16": 2, "bf16": 2, "e4m3fn": 1}
+
+
+def decode_bytes(case):
+    """Algorithmic bytes: attended K and V rows + Q read + O written."""
+    D, Hk, Hq = case["head_dim"], case["num_kv_heads"], case["num_q_heads"]
+    W = case["window"]
+    kv = 0
+    cu = case["cu_seqlens_q"]
+    for s, L in enumerate(case["seq_lens"]):
+        ql = int(cu[s + 1] - cu[s])
+        if ql == 0:
+            continue
+        # keys visible to at least one query of the sequence
+        first = (int(L) - ql - W + 1) if W > 0 else 0
+        kv += int(L) - max(0, first)
+    kvb = kv * Hk * D * EB[case["kv_dtype"]] * 2
+    tq = int(cu[-1])
+    return kvb + tq * Hq * D * (EB[case["q_dtype"]] + EB[case["o_dtype"]])
+
+
+def visible_pairs(case):
+    W = case["window"]
+    cu = case["cu_seqlens_q"]
+    n = 0
+    for s, L in enumerate(case["seq_lens"]):
+        ql = int(cu[s + 1] - cu[s])
+        ctx = int(L) - ql
+        for i in range(ql):
+            p = ctx + i
+            n += (p + 1) if W <= 0 else min(p + 1, W)
+    return n
+
+
+def prefill_flops(case):
+    return 4.0 * case["head_dim"] * case["num_q_heads"] * visible_pairs(case)
+
+
+class Runner:
+    """Pre-marshalled C-ABI calls for one device copy of a case."""
+
+    def __init__(self, case, dev, path="auto", n_part=0):
+        import torch
+        import paged_varlen_attention_ua_amd.attention as A
+        from paged_varlen_attention_ua_amd import binding as B
+        self.B = B
+        self.out = torch.empty_like(dev["q"])
+        self.prob = A.make_problem(
+            dev["q"], dev["k_cache"], dev["v_cache"], dev["block_table"],
+            num_seqs=len(case["seq_lens"]), max_seqlen_q=case["max_seqlen_q"],
+            max_seqlen_k=case["max_seqlen_k"], scale=case["scale"], softcap=case["softcap"],
+            window=case["window"], k_scale=case["k_scale"], v_scale=case["v_scale"],
+            alibi_slopes=dev["alibi_slopes"], sinks=dev["sinks"], out=self.out)
+        self.force = {"auto": B.UA_PATH_AUTO, "2d": B.UA_PATH_2D, "splitkv": B.UA_PATH_SPLITKV}[path]
+        self.n_part = n_part
+        self.ncu = A.num_cus(dev["q"].device)
+        self.plan = B.ua_plan(self.prob, self.ncu, self.force, n_part)
+        self.args = A.make_args(dev["q"], dev["k_cache"], dev["v_cache"], dev["block_table"],
+                                dev["cu_seqlens_q"], dev["seq_lens"], self.out,
+                                alibi_slopes=dev["alibi_slopes"], sinks=dev["sinks"])
+        nbytes = max(int(self.plan.workspace_bytes), 256)
+        self.ws = torch.empty(nbytes, dtype=torch.uint8, device=dev["q"].device)
+        self.ws_ptr = ctypes.c_void_p(self.ws.data_ptr())
+        self.ws_n = self.ws.numel()
+        self.dev = dev
+        self.lib = B.lib()
+        self.pp = ctypes.byref(self.prob)
+        self.pa = ctypes.byref(self.args)
+
+    def step(self, stream_ptr, ev=None):
+        """One pass: plan (host) + partition kernel (+ reduce).  ev = (start, end) events
+        recorded around the main kernel only."""
+        B, lib = self.B, self.lib
+        plan = B.UaPlan()
+        st = lib.ua_plan(self.pp, self.ncu, self.force, self.n_part, ctypes.byref(plan))
+        if st:
+            raise RuntimeError(f"ua_plan {st}")
+        pl = ctypes.byref(plan)
+        if ev is not None:
+            ev[0].record()
+        if plan.path == B.UA_PATH_2D:
+            st = lib.ua_forward_2d(self.pp, pl, self.pa, stream_ptr)
+            if ev is not None:
+                ev[1].record()
+        else:
+            st = lib.ua_forward_splitkv(self.pp, pl, self.pa, self.ws_ptr, self.ws_n, stream_ptr)
+            if ev is not None:
+                ev[1].record()
+            st = st or lib.ua_reduce(self.pp, pl, self.pa, self.ws_ptr, self.ws_n, stream_ptr)
+        if st:
+            raise RuntimeError(f"launch status {st}")
+
+
+def clone_dev(dev):
+    return {k: (v.clone() if v is not None else None) for k, v in dev.items()}
+
+
+def time_case(case, steps, warmup, path="auto", n_part=0, touched=None, kernel_events=True,
+              graph=True):
+    """Time one workload over R rotated input copies.
+
+    Eager pass: every step is launched from the host; HIP events on the launch
+    stream bracket the main kernel of each step (kernel_ms).  Graph pass: R
+    steps (one per input copy) are captured once into a HIP graph and replayed,
+    so the per-step time is the GPU's, not the Python launcher's (ms_per_step).
+    """
+    import torch
+    from tests.gpu_common import to_device
+    touched = touched or decode_bytes(case)
+    R = max(2, math.ceil((1 << 30) / max(touched, 1)))
+    R = min(R, 64)
+    base = to_device(case)
+    runners = [Runner(case, base, path, n_part)]
+    for _ in range(R - 1):
+        runners.append(Runner(case, clone_dev(base), path, n_part))
+    stream = torch.cuda.current_stream()
+    sp = ctypes.c_void_p(stream.cuda_stream)
+    for i in range(warmup):
+        runners[i % R].step(sp)
+    torch.cuda.synchronize()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(steps)] if kernel_events else None
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    t0.record()
+    for i in range(steps):
+        runners[i % R].step(sp, evs[i] if evs else None)
+    t1.record()
+    torch.cuda.synchronize()
+    eager_ms = t0.elapsed_time(t1) / steps
+    kms = (sum(a.elapsed_time(b) for a, b in evs) / steps) if evs else None
+    ms = eager_ms
+    if graph:
+        g = torch.cuda.CUDAGraph()
+        cs = torch.cuda.Stream()
+        cs.wait_stream(stream)
+        with torch.cuda.stream(cs):
+            for r in runners:  # one eager pass on the capture stream first
+                r.step(ctypes.c_void_p(cs.cuda_stream))
+        stream.wait_stream(cs)
+        torch.cuda.synchronize()
+        with torch.cuda.graph(g):
+            cap = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+            for r in runners:
+                r.step(cap)
+        for _ in range(max(1, warmup // R)):
+            g.replay()
+        torch.cuda.synchronize()
+        reps = max(1, math.ceil(steps / R))
+        t0.record()
+        for _ in range(reps):
+            g.replay()
+        t1.record()
+        torch.cuda.synchronize()
+        ms = t0.elapsed_time(t1) / (reps * R)
+    plan = runners[0].plan
+    return dict(ms_per_step=ms, eager_ms_per_step=eager_ms, kernel_ms=kms, path=int(plan.path),
+                n_part=int(plan.n_part), rotation_sets=R, kernel=int(plan.kernel))
+
+
+def kernel_source_digest():
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "paged_varlen_attention_ua_amd", "csrc")
+    for f in sorted(os.listdir(csrc)):
+        h.update(open(os.path.join(csrc, f), "rb").read())
+    return h.hexdigest()[:16]
+
+
+def traffic_entry(kernel_ms_per_launch):
+    """HBM bytes per launch from committed rocprofv3 counter summaries, if they
+    were taken on the current kernel sources; else None."""
+    path = os.path.join(ROOT, "profiles", "counters_split_kernel_long_decode.json")
+    try:
+        d = json.load(open(path))
+    except (OSError, ValueError):
+        return None
+    if d.get("kernel_source_digest") != kernel_source_digest():
+        return None
+    return d.get("traffic_bytes_per_launch")
+
+
+def cpu_baseline(case, budget_s=15.0):
+    """The oracle, untouched, on a bounded sample of the headline workload."""
+    import numpy as np
+    import oracle
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:
+        cores = os.cpu_count() or 1
+    n = len(case["seq_lens"])
+    done_bytes = 0
+    t0 = time.perf_counter()
+    reps = 0
+    while True:
+        for s in range(n):
+            cu = case["cu_seqlens_q"]
+            rows = np.arange(cu[s], cu[s + 1])
+            oracle.attention(**case, rows=rows)
+            sub = dict(case, seq_lens=case["seq_lens"][s:s + 1],
+                       cu_seqlens_q=np.array([0, cu[s + 1] - cu[s]], dtype=np.int32))
+            done_bytes += decode_bytes(sub)
+            if time.perf_counter() - t0 > budget_s:
+                break
+        reps += 1
+        if time.perf_counter() - t0 > budget_s:
+            break
+    dt = time.perf_counter() - t0
+    return {"value": round(done_bytes / dt / 1e9, 4), "unit": "GB/s", "cores": int(cores),
+            "kind": "oracle",
+            "sample": f"float64 numpy oracle over whole sequences of the headline workload, "
+                      f"{done_bytes / 1e6:.1f} MB of algorithmic bytes in {dt:.1f} s"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--quick", action="store_true", help="headline only (for profiling runs)")
+    ap.add_argument("--no-cpu", action="store_true", help="skip the cpu_baseline leg")
+    args = ap.parse_args()
+    ws = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or ws != 1:
+        print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1"}))
+        sys.exit(2)
+
+    import torch
+    from synth import WORKLOADS, make_case
+    torch.cuda.set_device(0)
+    torch.cuda.synchronize()
+
+    head = make_case(**WORKLOADS[HEADLINE], poison=False)
+    r = time_case(head, args.steps, args.warmup)
+    by = decode_bytes(head)
+    gbs = by / (r["ms_per_step"] * 1e-3) / 1e9
+    k_gbs = by / (r["kernel_ms"] * 1e-3) / 1e9
+    traffic = traffic_entry(r["kernel_ms"])
+    line = {
+        "metric": METRIC, "value": round(gbs, 2), "unit": "GB/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(r["ms_per_step"], 5),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "long-context split-KV decode: bf16, d128, 32q/8kv heads, "
+                               "block 16, batch 8, q_len 1, kv_len U[6500,6900], window 4096",
+                   "global_batch": 8, "seq_len": int(head["max_seqlen_k"]),
+                   "path": "splitkv" if r["path"] == 2 else "2d", "n_part": r["n_part"],
+                   "rotation_sets": r["rotation_sets"], "algorithmic_bytes": by,
+                   "timing": "HIP-graph replay of rotated steps; eager per-step ms "
+                             f"{r['eager_ms_per_step']:.5f}",
+                   "pct_hbm_peak": round(100 * gbs / HBM_PEAK_GBS, 2)},
+        "roofline": {"bound": "hbm", "achieved": round(k_gbs, 2), "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": round(k_gbs / HBM_PEAK_GBS, 4),
+                     "traffic": traffic,
+                     "kernel": "small_kernel (split-KV partitions)" if r["path"] == 2
+                     else "small_kernel (one pass)",
+                     "kernel_ms": round(r["kernel_ms"], 5)},
+    }
+    if not args.quick:
+        others = {}
+        for name in ["decode_fp16_d128_16q2kv", "fp8kv_decode_b32_ctx590",
+                     "fp8kv_decode_b8_ctx6700_w4096",
+                     "long_decode_bf16_d128_32q8kv_w4096_softcap_sinks"]:
+            c = make_case(**WORKLOADS[name], poison=False)
+            rr = time_case(c, args.steps, args.warmup, kernel_events=False)
+            b = decode_bytes(c)
+            v = b / (rr["ms_per_step"] * 1e-3) / 1e9
+            others[name] = {"GB/s": round(v, 2), "pct_hbm_peak": round(100 * v / HBM_PEAK_GBS, 2),
+                            "us_per_step": round(rr["ms_per_step"] * 1e3, 2),
+                            "path": "splitkv" if rr["path"] == 2 else "2d",
+                            "n_part": rr["n_part"]}
+        line["decode_other"] = others
+        pre = {}
+        for name in ["prefill_chunk1k_prefix8k_bf16", "prefill_chunk2k_prefix16k_bf16",
+                     "prefill_4x1k_bf16", "prefill_8k_d256_24q4kv_bs784_bf16"]:
+            c = make_case(**WORKLOADS[name], poison=False)
+            fl = prefill_flops(c)
+            rr = time_case(c, max(5, args.steps // 5), 3, touched=decode_bytes(c),
+                           kernel_events=False)
+            tf = fl / (rr["ms_per_step"] * 1e-3) / 1e12
+            pre[name] = {"TFLOP/s": round(tf, 2),
+                         "pct_mfma_peak": round(100 * tf / MFMA_PEAK_TFLOPS["bf16"], 2),
+                         "ms_per_step": round(rr["ms_per_step"], 4),
+                         "path": "splitkv" if rr["path"] == 2 else "2d",
+                         "kernel": "large" if rr["kernel"] == 1 else "small"}
+        line["prefill"] = pre
+        mixed = make_case(**WORKLOADS["mixed_fp16_d128_16q2kv"], poison=False)
+        rr = time_case(mixed, args.steps, args.warmup, kernel_events=False)
+        line["mixed_fp16_d128_16q2kv_us_per_step"] = round(rr["ms_per_step"] * 1e3, 2)
+    if not args.no_cpu:
+        line["cpu_baseline"] = cpu_baseline(make_case(**WORKLOADS[HEADLINE]))
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -81,7 +81,8 @@ ua_status validate(const ua_problem* p) {
   if (p->kv_stride_block % kv_vec || p->kv_stride_slot % kv_vec || p->kv_stride_head % kv_vec)
     return UA_EUNSUPPORTED;
   const int G = p->num_q_heads / p->num_kv_heads;
-  if (G > kSmallRows) return UA_EUNSUPPORTED;
+  if (G > kLargeRows) return UA_EUNSUPPORTED;
+  if (!(p->scale > 0.f)) return UA_EUNSUPPORTED;
   return UA_OK;
 }
 
@@ -193,8 +194,11 @@ ua_status ua_plan(const ua_problem* prob, int32_t num_cus, int32_t force_path,
   if (num_cus <= 0) num_cus = 256;
   std::memset(plan, 0, sizeof(*plan));
   const int G = prob->num_q_heads / prob->num_kv_heads;
-  plan->kernel = 0;
-  plan->block_q = kSmallRows / G;
+  // Small blocks (<= 16 rows, bandwidth-shaped) when every sequence's query
+  // run fits one of them; large MFMA blocks (128 rows) otherwise.
+  const bool small = G <= kSmallRows && (int64_t)prob->max_seqlen_q * G <= kSmallRows;
+  plan->kernel = small ? 0 : 1;
+  plan->block_q = small ? kSmallRows / G : kLargeRows / G;
   const int bq = plan->block_q;
   const int64_t slots = prob->num_seqs > 0 ? (int64_t)prob->total_q / bq + prob->num_seqs : 0;
   const int64_t est_blocks =
@@ -206,10 +210,15 @@ ua_status ua_plan(const ua_problem* prob, int32_t num_cus, int32_t force_path,
   // Automatic partition count: fill about four small workgroups per CU,
   // keep at least 256 keys per partition, and stay one-pass for short ranges.
   int auto_parts = 1;
-  if (wgs > 0 && eff_k > 1024) {
+  if (small && wgs > 0 && eff_k > 1024) {
     const int64_t want = ceil_div(4ll * num_cus, wgs);
     const int64_t by_len = std::max<int64_t>(1, eff_k / 256);
     auto_parts = (int)std::max<int64_t>(1, std::min<int64_t>(std::min(want, by_len), 64));
+  } else if (!small && wgs > 0 && wgs < num_cus && eff_k >= 4096) {
+    // Large blocks: split only a grid that underfills the device.
+    const int64_t want = ceil_div(2ll * num_cus, wgs);
+    const int64_t by_len = std::max<int64_t>(1, eff_k / 2048);
+    auto_parts = (int)std::max<int64_t>(1, std::min<int64_t>(std::min(want, by_len), 16));
   }
   int n_part;
   if (force_path == UA_PATH_2D) {

@@ -1,8 +1,390 @@
-// Large-query-block (prefill) kernel: not built yet.
+// Large-query-block attention kernel for gfx950: prefill and chunked prefill.
+//
+// One workgroup owns (query block, kv head, key partition); a query block is
+// block_q = 128 / G tokens times the G query heads of the kv head (grouped
+// rows share every K/V tile).  Four waves own 32 rows each.  Per 64-key tile
+// (32 keys for head dim 256):
+//   * the tile's K and V rows are gathered through the block table with
+//     16-byte loads into registers (next tile in flight while the current one
+//     is computed) and stored into double-buffered, XOR-swizzled LDS;
+//   * S^T = K Q^T on 32x32x16 MFMA (A = K from LDS, B = Q held in registers),
+//     so each lane owns one query row and 16 keys of each 32-key block;
+//   * online softmax in the base-2 domain (README section "2D vs 2D"), with
+//     the running maximum only moved when a tile's maximum exceeds it by more
+//     than 2^8 (exact up to rounding: every key of a row is scaled by the same
+//     maximum between moves, and p <= 256 stays representable);
+//   * causal, window and range masks are applied only on tiles that need them
+//     (the mask-phase split of the README's "BLOCK_M=128" section);
+//   * O^T = V^T P^T on 32x32x16 MFMA: P^T is already the B operand in the
+//     registers the S^T accumulator left it in, and V^T comes from
+//     ds_read_b64_tr_b16 transposed LDS reads (README "3D vs 3D").
+// Output: the final rows (one pass) or the partition's (m, l, acc) (split).
+
 #include "ua_device.h"
 
 namespace ua {
-hipError_t launch_large(const Params&, int, int, int, bool, dim3, hipStream_t) {
-  return hipErrorNotSupported;
+namespace {
+
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+
+// Transposed LDS read: within each 16-lane group, lane s gives the address of
+// 4 consecutive 16-bit values of row s/4 (columns 4(s%4)..+3) of a 4 x 16
+// block; lane i receives column i of the 4 rows.
+__device__ __forceinline__ u32x2 lds_read_tr16(const uint16_t* p) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+  s16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (lds_s16x4*)((__attribute__((address_space(3))) uint16_t*)(p)));
+  return __builtin_bit_cast(u32x2, v);
+#else
+  (void)p;
+  return u32x2{0, 0};
+#endif
 }
+
+template <int D>
+struct LargeCfg {
+  static constexpr int TK = D > 128 ? 32 : 64;  // keys per tile
+  static constexpr int NC = D / 8;               // 16-byte chunks per K/V row
+  static constexpr int KB = TK / 32;             // 32-key blocks per tile
+  static constexpr int QC = D / 16;              // QK MFMAs per 32-key block
+  static constexpr int DB = D / 32;              // PV output blocks of 32 head-dim rows
+  static constexpr int TILE = TK * D;            // elements per K (or V) tile
+  static constexpr int CPT = TK * NC / 256;      // 16-byte chunks per thread per tile
+};
+
+// Element offset of (key, 8-value chunk c) in a swizzled tile.
+template <int D>
+__device__ __forceinline__ int swz(int key, int c) {
+  constexpr int NC = LargeCfg<D>::NC;
+  return key * D + ((c ^ (key & (NC - 1))) << 3);
+}
+
+template <int QT, bool FP8, int D>
+struct Stage {
+  // FP8: 8 codes (2 dwords) per chunk; else 8 values (4 dwords) per chunk.
+  uint32_t k[LargeCfg<D>::CPT][FP8 ? 2 : 4];
+  uint32_t v[LargeCfg<D>::CPT][FP8 ? 2 : 4];
+};
+
+template <int QT, bool FP8, int D>
+__device__ __forceinline__ void stage_load(Stage<QT, FP8, D>& st, const Params& p,
+                                           const int32_t* __restrict__ bt_row, const char* kbase,
+                                           const char* vbase, int kt, int kl, int k1, int tid) {
+  using C = LargeCfg<D>;
+  constexpr int EB = FP8 ? 1 : 2;
+  const int64_t slot_b = p.kv_stride_slot * EB;
+  const int64_t blk_b = p.kv_stride_block * EB;
+#pragma unroll
+  for (int u = 0; u < C::CPT; ++u) {
+    const int i = tid + 256 * u;
+    const int key = i / C::NC, c = i % C::NC;
+    const int kk = kt + key;
+    if (kk >= kl && kk < k1) {
+      const uint32_t bi = fastdiv((uint32_t)kk, p.bs_div);
+      const int slot = kk - (int)bi * p.block_size;
+      const int64_t off = (int64_t)bt_row[bi] * blk_b + (int64_t)slot * slot_b + c * 8 * EB;
+      if constexpr (FP8) {
+        const u32x2 a = *reinterpret_cast<const u32x2*>(kbase + off);
+        const u32x2 b = *reinterpret_cast<const u32x2*>(vbase + off);
+        st.k[u][0] = a[0]; st.k[u][1] = a[1];
+        st.v[u][0] = b[0]; st.v[u][1] = b[1];
+      } else {
+        const u32x4 a = *reinterpret_cast<const u32x4*>(kbase + off);
+        const u32x4 b = *reinterpret_cast<const u32x4*>(vbase + off);
+#pragma unroll
+        for (int w = 0; w < 4; ++w) { st.k[u][w] = a[w]; st.v[u][w] = b[w]; }
+      }
+    } else {
+#pragma unroll
+      for (int w = 0; w < (FP8 ? 2 : 4); ++w) { st.k[u][w] = 0; st.v[u][w] = 0; }
+    }
+  }
+}
+
+template <int QT, bool FP8, int D>
+__device__ __forceinline__ void stage_store(const Stage<QT, FP8, D>& st, uint16_t* sk,
+                                            uint16_t* sv, int tid) {
+  using C = LargeCfg<D>;
+#pragma unroll
+  for (int u = 0; u < C::CPT; ++u) {
+    const int i = tid + 256 * u;
+    const int key = i / C::NC, c = i % C::NC;
+    u32x4 a, b;
+    if constexpr (FP8) {
+      a = fp8x8_to<QT>(u32x2{st.k[u][0], st.k[u][1]});
+      b = fp8x8_to<QT>(u32x2{st.v[u][0], st.v[u][1]});
+    } else {
+      a = u32x4{st.k[u][0], st.k[u][1], st.k[u][2], st.k[u][3]};
+      b = u32x4{st.v[u][0], st.v[u][1], st.v[u][2], st.v[u][3]};
+    }
+    *reinterpret_cast<u32x4*>(sk + swz<D>(key, c)) = a;
+    *reinterpret_cast<u32x4*>(sv + swz<D>(key, c)) = b;
+  }
+}
+
+template <int QT, bool FP8, int D, bool SPLIT>
+__global__ __launch_bounds__(256, (D > 128 ? 1 : 2)) void large_kernel(Params p) {
+  using C = LargeCfg<D>;
+  constexpr int TK = C::TK;
+  __shared__ __attribute__((aligned(16))) uint16_t sK[2][C::TILE];
+  __shared__ __attribute__((aligned(16))) uint16_t sV[2][C::TILE];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6;
+  const int l32 = lane & 31, g2 = lane >> 5;
+
+  // XCD-aware order: consecutive logical blocks (the query blocks of one kv
+  // head and partition, which read the same K/V) stay on one XCD; heavier
+  // (later) query blocks go first.
+  const int gx = gridDim.x, gy = gridDim.y;
+  const int nwg = gx * gy * gridDim.z;
+  int lin = blockIdx.x + gx * (blockIdx.y + gy * blockIdx.z);
+  if ((nwg & 7) == 0) lin = (lin & 7) * (nwg >> 3) + (lin >> 3);
+  const int qb = gx - 1 - (lin % gx);
+  const int kvh = (lin / gx) % gy;
+  const int part = lin / (gx * gy);
+
+  const int s = find_seq(p.cu_seqlens_q, p.num_seqs, qb, p.block_q);
+  const int q_start = p.cu_seqlens_q[s], q_end = p.cu_seqlens_q[s + 1];
+  const int tok0 = q_start + (qb - (q_start / p.block_q + s)) * p.block_q;
+  if (tok0 >= q_end) return;
+  const int ntok = min(p.block_q, q_end - tok0);
+  const int kv_len = p.seq_lens[s];
+  const int ctx = kv_len - (q_end - q_start);
+  const int p0 = ctx + (tok0 - q_start);
+  const int hi = p0 + ntok;
+  const int lo = p.window > 0 ? max(0, p0 - p.window + 1) : 0;
+  const int lo_a = (lo / TK) * TK;
+  const int plen = ((hi - lo_a + p.n_part - 1) / p.n_part + TK - 1) / TK * TK;
+  const int k0 = lo_a + part * plen;
+  const int k1 = min(k0 + plen, hi);
+  const int kl = max(k0, lo);
+  const int G = p.group;
+  const int R = p.total_q * p.num_q_heads;
+  const int nrows = p.block_q * G;
+
+  // This lane's row (wave owns rows 32*wave .. 32*wave + 31).
+  const int row = 32 * wave + l32;
+  const int rt = row / G, rh = row - rt * G;
+  const bool row_ok = row < nrows && rt < ntok;
+  const int h = kvh * G + rh;
+  const int pos = p0 + rt;
+
+  if (k0 >= k1) {
+    if constexpr (SPLIT) {
+      if (g2 == 0 && row_ok) {
+        const int64_t rr = (int64_t)(tok0 + rt) * p.num_q_heads + h;
+        p.ws_l[(int64_t)part * R + rr] = 0.0f;
+        p.ws_m[(int64_t)part * R + rr] = -INFINITY;
+      }
+    }
+    return;
+  }
+
+  // Wave-uniform position range of this wave's rows, for the mask-free test.
+  const int w_row0 = 32 * wave;
+  const int w_rowl = min(32 * wave + 31, nrows - 1);
+  const int wave_pmin = p0 + min(w_row0 / G, ntok - 1);
+  const int wave_pmax = p0 + min(w_rowl / G, ntok - 1);
+  const bool wave_live = w_row0 < nrows && w_row0 / G < ntok;
+
+  const int row_lo = p.window > 0 ? max(kl, pos - p.window + 1) : kl;
+  const int row_hi = min(k1, pos + 1);
+  const float slope2 = (p.alibi != nullptr && row_ok) ? p.alibi[h] * kLog2e : 0.0f;
+  const bool general = p.softcap_on || p.alibi != nullptr;
+
+  // Q as the B operand of S^T = K Q^T: lane holds Q[row][16c + 8*g2 .. + 8].
+  u32x4 qop[C::QC];
+  if (row_ok) {
+    const char* qp = reinterpret_cast<const char*>(p.q) +
+                     ((int64_t)(tok0 + rt) * p.q_stride_tok + (int64_t)h * p.q_stride_head) * 2;
+#pragma unroll
+    for (int c = 0; c < C::QC; ++c)
+      qop[c] = *reinterpret_cast<const u32x4*>(qp + (16 * c + 8 * g2) * 2);
+  } else {
+#pragma unroll
+    for (int c = 0; c < C::QC; ++c) qop[c] = u32x4{0, 0, 0, 0};
+  }
+
+  const int32_t* bt_row = p.block_table + (int64_t)s * p.max_blocks_per_seq;
+  constexpr int EB = FP8 ? 1 : 2;
+  const char* kbase = reinterpret_cast<const char*>(p.k) + kvh * p.kv_stride_head * EB;
+  const char* vbase = reinterpret_cast<const char*>(p.v) + kvh * p.kv_stride_head * EB;
+
+  f32x16 oacc[C::DB];
+#pragma unroll
+  for (int d = 0; d < C::DB; ++d) oacc[d] = f32x16{};
+  float m_run = -INFINITY, l_run = 0.0f;
+  const float c2 = p.qk_scale2;
+
+  const int ntiles = (k1 - k0 + TK - 1) / TK;
+  Stage<QT, FP8, D> st;
+  stage_load<QT, FP8, D>(st, p, bt_row, kbase, vbase, k0, kl, k1, tid);
+  stage_store<QT, FP8, D>(st, sK[0], sV[0], tid);
+  __syncthreads();
+
+  for (int t = 0; t < ntiles; ++t) {
+    const int kt = k0 + t * TK;
+    const int buf = t & 1;
+    if (t + 1 < ntiles) stage_load<QT, FP8, D>(st, p, bt_row, kbase, vbase, kt + TK, kl, k1, tid);
+
+    if (wave_live) {
+      const uint16_t* sk = sK[buf];
+      const uint16_t* sv = sV[buf];
+      // ---- S^T = K Q^T
+      f32x16 sacc[C::KB];
+#pragma unroll
+      for (int kb = 0; kb < C::KB; ++kb) {
+        sacc[kb] = f32x16{};
+        const int key = 32 * kb + l32;
+#pragma unroll
+        for (int c = 0; c < C::QC; ++c) {
+          const u32x4 a = *reinterpret_cast<const u32x4*>(sk + swz<D>(key, 2 * c + g2));
+          sacc[kb] = mfma32<QT>(a, qop[c], sacc[kb]);
+        }
+      }
+      // ---- logits (base 2) and masks
+      const bool full = !general && kt >= kl && kt + TK <= k1 && kt + TK - 1 <= wave_pmin &&
+                        (p.window <= 0 || kt > wave_pmax - p.window);
+      float mt = -INFINITY;
+      if (full) {
+#pragma unroll
+        for (int kb = 0; kb < C::KB; ++kb)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            sacc[kb][r] *= c2;
+            mt = fmaxf(mt, sacc[kb][r]);
+          }
+      } else {
+#pragma unroll
+        for (int kb = 0; kb < C::KB; ++kb)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int key = kt + 32 * kb + 8 * (r >> 2) + 4 * g2 + (r & 3);
+            const float raw = sacc[kb][r];
+            float v = p.softcap_on ? p.cap_out2 * tanh_fast(raw * p.cap_in) : raw * c2;
+            v += slope2 * (float)(key - ctx);
+            v = (key >= row_lo && key < row_hi) ? v : -INFINITY;
+            sacc[kb][r] = v;
+            mt = fmaxf(mt, v);
+          }
+      }
+      // Row maximum across the lane pair (l, l ^ 32) holding the same row.
+      mt = wave_max_xor(mt, 32);
+      // Move the running maximum only when this tile exceeds it by > 8 (base 2).
+      const bool need = mt > m_run + 8.0f;
+      if (__builtin_amdgcn_ballot_w64(need)) {
+        const float m_new = need ? mt : m_run;
+        const float alpha = need ? fast_exp2(m_run - m_new) : 1.0f;  // m_run = -inf -> 0
+        l_run *= alpha;
+#pragma unroll
+        for (int d = 0; d < C::DB; ++d) oacc[d] *= alpha;
+        m_run = m_new;
+      }
+      const float m_use = (m_run == -INFINITY) ? 0.0f : m_run;
+      // ---- P = 2^(x - m), packed as the B operands of the PV MFMAs
+      u32x4 pop[TK / 16];
+      float psum = 0.0f;
+#pragma unroll
+      for (int kk = 0; kk < TK / 16; ++kk) {
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const float a = fast_exp2(sacc[kk >> 1][8 * (kk & 1) + 2 * q] - m_use);
+          const float b = fast_exp2(sacc[kk >> 1][8 * (kk & 1) + 2 * q + 1] - m_use);
+          psum += a + b;
+          pop[kk][q] = pack2<QT>(a, b);
+        }
+      }
+      l_run += psum;
+      // ---- O^T += V^T P^T
+      const int s16 = lane & 15, q16 = lane >> 4;
+#pragma unroll
+      for (int d = 0; d < C::DB; ++d) {
+        const int dcol = 32 * d + 16 * (q16 & 1) + 4 * (s16 & 3);
+#pragma unroll
+        for (int kk = 0; kk < TK / 16; ++kk) {
+          const int key0 = 16 * kk + 4 * g2 + (s16 >> 2);
+          const u32x2 lo2 = lds_read_tr16(sv + swz<D>(key0, dcol >> 3) + (dcol & 7));
+          const u32x2 hi2 = lds_read_tr16(sv + swz<D>(key0 + 8, dcol >> 3) + (dcol & 7));
+          oacc[d] = mfma32<QT>(u32x4{lo2[0], lo2[1], hi2[0], hi2[1]}, pop[kk], oacc[d]);
+        }
+      }
+    }
+    if (t + 1 < ntiles) stage_store<QT, FP8, D>(st, sK[buf ^ 1], sV[buf ^ 1], tid);
+    __syncthreads();
+  }
+
+  if (!row_ok) return;
+  // Lanes l and l ^ 32 hold the same row: total l.
+  l_run = wave_sum_xor(l_run, 32);
+  const int tok = tok0 + rt;
+  const int64_t rrow = (int64_t)tok * p.num_q_heads + h;
+  // O^T accumulator: register r of block d holds O[row][32d + 8(r/4) + 4*g2 + r%4].
+  if constexpr (SPLIT) {
+    if (g2 == 0) {
+      p.ws_m[(int64_t)part * R + rrow] = (l_run > 0.0f) ? m_run : -INFINITY;
+      p.ws_l[(int64_t)part * R + rrow] = l_run;
+    }
+    float* dst = p.ws_acc + ((int64_t)part * R + rrow) * D;
+#pragma unroll
+    for (int d = 0; d < C::DB; ++d)
+#pragma unroll
+      for (int r4 = 0; r4 < 4; ++r4)
+        *reinterpret_cast<f32x4*>(dst + 32 * d + 8 * r4 + 4 * g2) =
+            f32x4{oacc[d][4 * r4], oacc[d][4 * r4 + 1], oacc[d][4 * r4 + 2], oacc[d][4 * r4 + 3]};
+  } else {
+    const float sink2 = p.sinks != nullptr ? p.sinks[h] * kLog2e : -INFINITY;
+    const float Mt = fmaxf(m_run, sink2);
+    const float Ms = (Mt == -INFINITY) ? 0.0f : Mt;
+    const float f = fast_exp2(m_run - Ms);
+    float L = l_run * f;
+    const bool any_key = L > 0.0f;
+    if (sink2 != -INFINITY) L += fast_exp2(sink2 - Ms);
+    const float inv = any_key ? p.v_scale * f / L : 0.0f;
+    char* dst = reinterpret_cast<char*>(p.out) +
+                ((int64_t)tok * p.o_stride_tok + (int64_t)h * p.o_stride_head) * 2;
+#pragma unroll
+    for (int d = 0; d < C::DB; ++d)
+#pragma unroll
+      for (int r4 = 0; r4 < 4; ++r4)
+        *reinterpret_cast<u32x2*>(dst + (32 * d + 8 * r4 + 4 * g2) * 2) =
+            u32x2{pack2<QT>(oacc[d][4 * r4] * inv, oacc[d][4 * r4 + 1] * inv),
+                  pack2<QT>(oacc[d][4 * r4 + 2] * inv, oacc[d][4 * r4 + 3] * inv)};
+    if (p.lse != nullptr && g2 == 0)
+      p.lse[rrow] = (L > 0.0f) ? (Ms + fast_log2(L)) * kLn2 : -INFINITY;
+  }
+}
+
+template <int QT, bool FP8, int D>
+hipError_t launch_large_t(const Params& p, bool split, dim3 grid, hipStream_t stream) {
+  if (split)
+    hipLaunchKernelGGL((large_kernel<QT, FP8, D, true>), grid, dim3(256), 0, stream, p);
+  else
+    hipLaunchKernelGGL((large_kernel<QT, FP8, D, false>), grid, dim3(256), 0, stream, p);
+  return hipGetLastError();
+}
+
+template <int QT, bool FP8>
+hipError_t launch_large_d(const Params& p, int head_dim, bool split, dim3 grid,
+                          hipStream_t stream) {
+  switch (head_dim) {
+    case 64: return launch_large_t<QT, FP8, 64>(p, split, grid, stream);
+    case 128: return launch_large_t<QT, FP8, 128>(p, split, grid, stream);
+    case 256: return launch_large_t<QT, FP8, 256>(p, split, grid, stream);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+}  // namespace
+
+hipError_t launch_large(const Params& p, int q_dtype, int kv_fp8, int head_dim, bool split,
+                        dim3 grid, hipStream_t stream) {
+  if (q_dtype == UA_F16)
+    return kv_fp8 ? launch_large_d<UA_F16, true>(p, head_dim, split, grid, stream)
+                  : launch_large_d<UA_F16, false>(p, head_dim, split, grid, stream);
+  return kv_fp8 ? launch_large_d<UA_BF16, true>(p, head_dim, split, grid, stream)
+                : launch_large_d<UA_BF16, false>(p, head_dim, split, grid, stream);
+}
+
 }  // namespace ua

@@ -12,10 +12,15 @@
 namespace ua {
 namespace {
 
+// One 64-thread workgroup per (row group): TPR threads own 4 head-dim values
+// of a row each.  All partition states are fetched before any is used (no
+// data-dependent branch between loads), so a row costs about two memory
+// round trips whatever the partition count.
 template <int OT, int D>
-__global__ __launch_bounds__(256) void reduce_kernel(Params p) {
-  constexpr int TPR = D / 4;            // threads per row, 4 values each
-  constexpr int RPB = 256 / TPR;        // rows per block
+__global__ __launch_bounds__(64) void reduce_kernel(Params p) {
+  constexpr int TPR = D / 4;          // threads per row, 4 values each
+  constexpr int RPB = 64 / TPR;       // rows per workgroup
+  constexpr int U = 8;                // partitions fetched per batch
   const int R = p.total_q * p.num_q_heads;
   const int tid = threadIdx.x;
   const int64_t row = (int64_t)blockIdx.x * RPB + tid / TPR;
@@ -25,22 +30,40 @@ __global__ __launch_bounds__(256) void reduce_kernel(Params p) {
   const int P = p.n_part;
 
   float M = -INFINITY;
-  for (int q = 0; q < P; ++q) {
-    const float l = p.ws_l[(int64_t)q * R + row];
-    if (l > 0.0f) M = fmaxf(M, p.ws_m[(int64_t)q * R + row]);
+  for (int q0 = 0; q0 < P; q0 += U) {
+    float mv[U], lv[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int q = q0 + u;
+      mv[u] = q < P ? p.ws_m[(int64_t)q * R + row] : -INFINITY;
+      lv[u] = q < P ? p.ws_l[(int64_t)q * R + row] : 0.0f;
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) M = lv[u] > 0.0f ? fmaxf(M, mv[u]) : M;
   }
   const float sink2 = (p.sinks != nullptr) ? p.sinks[h] * kLog2e : -INFINITY;
   const float Mt = fmaxf(M, sink2);
   const float Ms = (Mt == -INFINITY) ? 0.0f : Mt;
   float L = 0.0f;
   f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-  for (int q = 0; q < P; ++q) {
-    const float l = p.ws_l[(int64_t)q * R + row];
-    if (l > 0.0f) {
-      const float w = fast_exp2(p.ws_m[(int64_t)q * R + row] - Ms);
-      L += w * l;
-      const f32x4 a = *reinterpret_cast<const f32x4*>(p.ws_acc + ((int64_t)q * R + row) * D + d0);
-      acc += w * a;
+  for (int q0 = 0; q0 < P; q0 += U) {
+    float mv[U], lv[U];
+    f32x4 av[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int q = q0 + u;
+      mv[u] = q < P ? p.ws_m[(int64_t)q * R + row] : 0.0f;
+      lv[u] = q < P ? p.ws_l[(int64_t)q * R + row] : 0.0f;
+      av[u] = q < P ? *reinterpret_cast<const f32x4*>(p.ws_acc + ((int64_t)q * R + row) * D + d0)
+                    : f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const bool live = lv[u] > 0.0f;  // l == 0: acc and m are unspecified, never used
+      const float w = live ? fast_exp2(mv[u] - Ms) : 0.0f;
+      L += w * lv[u];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) acc[e] += live ? w * av[u][e] : 0.0f;
     }
   }
   const bool any_key = L > 0.0f;
@@ -60,16 +83,15 @@ hipError_t launch_reduce_t(const Params& p, int head_dim, hipStream_t stream) {
   if (R == 0) return hipSuccess;
   switch (head_dim) {
     case 64:
-      hipLaunchKernelGGL((reduce_kernel<OT, 64>), dim3((unsigned)((R + 15) / 16)), dim3(256), 0,
+      hipLaunchKernelGGL((reduce_kernel<OT, 64>), dim3((unsigned)((R + 3) / 4)), dim3(64), 0,
                          stream, p);
       break;
     case 128:
-      hipLaunchKernelGGL((reduce_kernel<OT, 128>), dim3((unsigned)((R + 7) / 8)), dim3(256), 0,
+      hipLaunchKernelGGL((reduce_kernel<OT, 128>), dim3((unsigned)((R + 1) / 2)), dim3(64), 0,
                          stream, p);
       break;
     case 256:
-      hipLaunchKernelGGL((reduce_kernel<OT, 256>), dim3((unsigned)((R + 3) / 4)), dim3(256), 0,
-                         stream, p);
+      hipLaunchKernelGGL((reduce_kernel<OT, 256>), dim3((unsigned)R), dim3(64), 0, stream, p);
       break;
     default:
       return hipErrorInvalidValue;
