@@ -202,17 +202,67 @@ def kernel_source_digest():
     return h.hexdigest()[:16]
 
 
-def traffic_entry(kernel_ms_per_launch):
-    """HBM bytes per launch from committed rocprofv3 counter summaries, if they
-    were taken on the current kernel sources; else None."""
-    path = os.path.join(ROOT, "profiles", "counters_split_kernel_long_decode.json")
+def traffic_entry():
+    """HBM bytes per launch from the committed rocprofv3 counter summary, if it
+    was taken on the current kernel sources; else None."""
     try:
-        d = json.load(open(path))
+        d = json.load(open(COUNTERS_JSON))
     except (OSError, ValueError):
         return None
     if d.get("kernel_source_digest") != kernel_source_digest():
         return None
     return d.get("traffic_bytes_per_launch")
+
+
+COUNTERS_JSON = os.path.join(ROOT, "profiles", "counters_split_kernel_long_decode.json")
+COPY_BYTES = 256 << 20
+
+
+def calib_copy():
+    """One elementwise pass reading COPY_BYTES and writing COPY_BYTES (torch's
+    neg kernel, a name no other kernel of the run has): the known-size kernel
+    whose FETCH_SIZE / WRITE_SIZE calibrate the counters."""
+    import torch
+    a = torch.ones(COPY_BYTES // 4, dtype=torch.float32, device="cuda")
+    b = torch.empty_like(a)
+    torch.cuda.synchronize()
+    torch.neg(a, out=b)
+    torch.cuda.synchronize()
+
+
+def summarize_pmc(fetch_csv, write_csv, kernel_substr="small_kernel"):
+    """Turn two rocprofv3 --pmc counter_collection.csv files (FETCH_SIZE run,
+    WRITE_SIZE run, both of `bench.py --quick --calib-copy`) into HBM bytes per
+    launch of the main kernel, scaled by the copy kernel's counters."""
+    import csv
+    def per_kernel(path, counter):
+        acc = {}
+        for r in csv.DictReader(open(path)):
+            if r.get("Counter_Name") != counter:
+                continue
+            acc.setdefault(r["Kernel_Name"], []).append(float(r["Counter_Value"]))
+        return acc
+    f = per_kernel(fetch_csv, "FETCH_SIZE")
+    w = per_kernel(write_csv, "WRITE_SIZE")
+    def pick(d, key):
+        ks = [k for k in d if key in k]
+        vals = [v for k in ks for v in d[k]]
+        return (sum(vals) / len(vals)) if vals else None, len(vals)
+    copy_f, _ = pick(f, "neg_kernel")
+    copy_w, _ = pick(w, "neg_kernel")
+    kf, nf = pick(f, kernel_substr)
+    kw, nw = pick(w, kernel_substr)
+    fr = COPY_BYTES / (copy_f * 1024.0)
+    fw = COPY_BYTES / (copy_w * 1024.0)
+    out = {"kernel_source_digest": kernel_source_digest(),
+           "kernel": kernel_substr, "dispatches": [nf, nw],
+           "fetch_kib_per_dispatch": kf, "write_kib_per_dispatch": kw,
+           "copy_fetch_kib": copy_f, "copy_write_kib": copy_w,
+           "copy_bytes": COPY_BYTES, "read_scale": fr, "write_scale": fw,
+           "traffic_bytes_per_launch": kf * 1024.0 * fr + kw * 1024.0 * fw}
+    os.makedirs(os.path.dirname(COUNTERS_JSON), exist_ok=True)
+    json.dump(out, open(COUNTERS_JSON, "w"), indent=1)
+    print(json.dumps(out))
 
 
 def cpu_baseline(case, budget_s=15.0):
@@ -254,8 +304,17 @@ def main():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--quick", action="store_true", help="headline only (for profiling runs)")
+    ap.add_argument("--workload", default=None,
+                    help="with --quick: time this named workload instead (profiling runs)")
     ap.add_argument("--no-cpu", action="store_true", help="skip the cpu_baseline leg")
+    ap.add_argument("--calib-copy", action="store_true",
+                    help="run one copy of known size first (PMC calibration)")
+    ap.add_argument("--summarize-pmc", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
+                    help="write profiles/ counters JSON from two rocprofv3 --pmc runs")
     args = ap.parse_args()
+    if args.summarize_pmc:
+        summarize_pmc(*args.summarize_pmc)
+        return
     ws = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or ws != 1:
         print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1"}))
@@ -266,12 +325,25 @@ def main():
     torch.cuda.set_device(0)
     torch.cuda.synchronize()
 
+    if args.calib_copy:
+        calib_copy()
+    if args.quick and args.workload and args.workload != HEADLINE:
+        c = make_case(**WORKLOADS[args.workload], poison=False)
+        rr = time_case(c, args.steps, args.warmup, touched=decode_bytes(c))
+        rec = {"workload": args.workload, "ms_per_step": rr["ms_per_step"],
+               "kernel_ms": rr["kernel_ms"], "path": rr["path"], "n_part": rr["n_part"],
+               "kernel": rr["kernel"]}
+        if c["max_seqlen_q"] > 1:
+            rec["TFLOP/s"] = prefill_flops(c) / (rr["ms_per_step"] * 1e-3) / 1e12
+        rec["GB/s"] = decode_bytes(c) / (rr["ms_per_step"] * 1e-3) / 1e9
+        print(json.dumps(rec), flush=True)
+        return
     head = make_case(**WORKLOADS[HEADLINE], poison=False)
     r = time_case(head, args.steps, args.warmup)
     by = decode_bytes(head)
     gbs = by / (r["ms_per_step"] * 1e-3) / 1e9
     k_gbs = by / (r["kernel_ms"] * 1e-3) / 1e9
-    traffic = traffic_entry(r["kernel_ms"])
+    traffic = traffic_entry()
     line = {
         "metric": METRIC, "value": round(gbs, 2), "unit": "GB/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(r["ms_per_step"], 5),

@@ -214,10 +214,11 @@ ua_status ua_plan(const ua_problem* prob, int32_t num_cus, int32_t force_path,
     const int64_t want = ceil_div(4ll * num_cus, wgs);
     const int64_t by_len = std::max<int64_t>(1, eff_k / 256);
     auto_parts = (int)std::max<int64_t>(1, std::min<int64_t>(std::min(want, by_len), 64));
-  } else if (!small && wgs > 0 && wgs < num_cus && eff_k >= 4096) {
-    // Large blocks: split only a grid that underfills the device.
+  } else if (!small && wgs > 0 && wgs < 2ll * num_cus && eff_k >= 1024) {
+    // Large blocks run two per CU: split a grid that does not fill that,
+    // keeping at least 512 keys per partition.
     const int64_t want = ceil_div(2ll * num_cus, wgs);
-    const int64_t by_len = std::max<int64_t>(1, eff_k / 2048);
+    const int64_t by_len = std::max<int64_t>(1, eff_k / 512);
     auto_parts = (int)std::max<int64_t>(1, std::min<int64_t>(std::min(want, by_len), 16));
   }
   int n_part;
