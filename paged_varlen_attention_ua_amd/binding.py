@@ -46,7 +46,7 @@ class UaPlan(ctypes.Structure):
     _fields_ = [
         ("path", ctypes.c_int32), ("kernel", ctypes.c_int32), ("block_q", ctypes.c_int32),
         ("n_part", ctypes.c_int32), ("grid_x", ctypes.c_int32), ("grid_y", ctypes.c_int32),
-        ("grid_z", ctypes.c_int32), ("reserved", ctypes.c_int32),
+        ("grid_z", ctypes.c_int32), ("flags", ctypes.c_int32),
         ("workspace_bytes", ctypes.c_uint64), ("problem_hash", ctypes.c_uint64),
     ]
 

@@ -161,6 +161,7 @@ Params make_params(const ua_problem* p, const ua_plan_t* plan, const ua_args* a,
   }
   q.v_scale = fp8 ? p->v_scale : 1.0f;
   q.grid_x = plan->grid_x;
+  q.seq_blocks = plan->flags & 1;
   return q;
 }
 
@@ -210,8 +211,11 @@ ua_status ua_plan(const ua_problem* prob, int32_t num_cus, int32_t force_path,
   // Automatic partition count: fill about four small workgroups per CU,
   // keep at least 256 keys per partition, and stay one-pass for short ranges.
   int auto_parts = 1;
-  if (small && wgs > 0 && eff_k > 1024) {
-    const int64_t want = ceil_div(4ll * num_cus, wgs);
+  if (small && wgs > 0 && wgs < num_cus && eff_k > 1024) {
+    // Measured on MI355X: about one small workgroup per CU for 16-bit KV and two
+    // for fp8 KV (half the bytes per key), at least 256 keys per partition.
+    const int64_t per_cu = prob->kv_dtype == UA_FP8_E4M3FN ? 2 : 1;
+    const int64_t want = ceil_div(per_cu * num_cus, wgs);
     const int64_t by_len = std::max<int64_t>(1, eff_k / 256);
     auto_parts = (int)std::max<int64_t>(1, std::min<int64_t>(std::min(want, by_len), 64));
   } else if (!small && wgs > 0 && wgs < 2ll * num_cus && eff_k >= 1024) {
@@ -235,6 +239,11 @@ ua_status ua_plan(const ua_problem* prob, int32_t num_cus, int32_t force_path,
   plan->n_part = n_part;
   if (slots > 0x7fffffff) return UA_EUNSUPPORTED;
   plan->grid_x = (int32_t)slots;
+  // Every sequence's query run fits one block: block x is the sequence index.
+  if (prob->max_seqlen_q <= bq) {
+    plan->flags |= 1;
+    plan->grid_x = prob->num_seqs;
+  }
   plan->grid_y = prob->num_kv_heads;
   plan->grid_z = n_part;
   plan->workspace_bytes =

@@ -112,7 +112,7 @@ __device__ __forceinline__ float fast_rcp(float x) { return __builtin_amdgcn_rcp
 // tanh from one base-2 exponential: tanh|x| = (1 - e) / (1 + e), e = 2^(-2|x| log2 e).
 __device__ __forceinline__ float tanh_fast(float x) {
   float e = fast_exp2(-2.0f * kLog2e * __builtin_fabsf(x));
-  float t = (1.0f - e) / (1.0f + e);
+  float t = (1.0f - e) * fast_rcp(1.0f + e);
   return __builtin_copysignf(t, x);
 }
 

@@ -70,6 +70,7 @@ struct Params {
   float v_scale;        // fp8 value scale (1 otherwise)
   int32_t softcap_on;
   int32_t grid_x;       // number of query-block slots launched along x
+  int32_t seq_blocks;   // 1: block x is the sequence index (every query run fits one block)
 };
 
 // Launchers (defined next to their kernels).  Return hipError_t of the launch.

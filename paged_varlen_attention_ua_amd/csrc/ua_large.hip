@@ -4,15 +4,20 @@
 // block_q = 128 / G tokens times the G query heads of the kv head (grouped
 // rows share every K/V tile).  Four waves own 32 rows each.  Per 64-key tile
 // (32 keys for head dim 256):
-//   * the tile's K and V rows are gathered through the block table with
-//     16-byte loads into registers (next tile in flight while the current one
-//     is computed) and stored into double-buffered, XOR-swizzled LDS;
+//   * the tile's K and V rows are gathered through the block table (its entries
+//     for the workgroup's key range are staged in LDS once) with 16-byte loads
+//     into registers, the next tile in flight while the current one is
+//     computed, and stored into double-buffered LDS rows padded to D + 16
+//     values (no bank conflicts for either read pattern below, and every read
+//     address is a per-lane base plus a constant);
 //   * S^T = K Q^T on 32x32x16 MFMA (A = K from LDS, B = Q held in registers),
 //     so each lane owns one query row and 16 keys of each 32-key block;
-//   * online softmax in the base-2 domain (README section "2D vs 2D"), with
-//     the running maximum only moved when a tile's maximum exceeds it by more
-//     than 2^8 (exact up to rounding: every key of a row is scaled by the same
-//     maximum between moves, and p <= 256 stays representable);
+//   * online softmax in the base-2 domain (README section "2D vs 2D") on the
+//     raw dot products (the logit scale is applied inside the one FMA that
+//     feeds exp2), with the running maximum only moved when a tile's maximum
+//     exceeds it by more than 2^8 (exact up to rounding: every key of a row is
+//     scaled by the same maximum between moves, and p <= 256 stays
+//     representable);
 //   * causal, window and range masks are applied only on tiles that need them
 //     (the mask-phase split of the README's "BLOCK_M=128" section);
 //   * O^T = V^T P^T on 32x32x16 MFMA: P^T is already the B operand in the
@@ -49,15 +54,19 @@ struct LargeCfg {
   static constexpr int KB = TK / 32;             // 32-key blocks per tile
   static constexpr int QC = D / 16;              // QK MFMAs per 32-key block
   static constexpr int DB = D / 32;              // PV output blocks of 32 head-dim rows
-  static constexpr int TILE = TK * D;            // elements per K (or V) tile
+  static constexpr int PITCH = D + 16;           // LDS row pitch in 16-bit values
+  static constexpr int TILE = TK * PITCH;        // values per K (or V) tile buffer
   static constexpr int CPT = TK * NC / 256;      // 16-byte chunks per thread per tile
+  static constexpr int MAXPG = 1024;             // block-table entries staged in LDS
 };
 
-// Element offset of (key, 8-value chunk c) in a swizzled tile.
+// Offset (in 16-bit values) of (key, 8-value chunk c) in a tile buffer.  With
+// a pitch of D + 16 values, consecutive rows start 32 bytes (8 banks) apart:
+// 8 keys reading the same 16-byte chunk, and 4 keys reading one 32-byte piece
+// (the transposed reads), touch disjoint banks.
 template <int D>
-__device__ __forceinline__ int swz(int key, int c) {
-  constexpr int NC = LargeCfg<D>::NC;
-  return key * D + ((c ^ (key & (NC - 1))) << 3);
+__device__ __forceinline__ int lds_off(int key, int c) {
+  return key * LargeCfg<D>::PITCH + c * 8;
 }
 
 template <int QT, bool FP8, int D>
@@ -67,9 +76,12 @@ struct Stage {
   uint32_t v[LargeCfg<D>::CPT][FP8 ? 2 : 4];
 };
 
+// Gather one tile's K/V chunks into registers.  `pg` holds the block-table
+// entries of blocks pg_first .. pg_first + MAXPG - 1 (the workgroup's range).
 template <int QT, bool FP8, int D>
 __device__ __forceinline__ void stage_load(Stage<QT, FP8, D>& st, const Params& p,
-                                           const int32_t* __restrict__ bt_row, const char* kbase,
+                                           const int32_t* __restrict__ bt_row,
+                                           const int32_t* pg, int pg_first, const char* kbase,
                                            const char* vbase, int kt, int kl, int k1, int tid) {
   using C = LargeCfg<D>;
   constexpr int EB = FP8 ? 1 : 2;
@@ -83,7 +95,9 @@ __device__ __forceinline__ void stage_load(Stage<QT, FP8, D>& st, const Params& 
     if (kk >= kl && kk < k1) {
       const uint32_t bi = fastdiv((uint32_t)kk, p.bs_div);
       const int slot = kk - (int)bi * p.block_size;
-      const int64_t off = (int64_t)bt_row[bi] * blk_b + (int64_t)slot * slot_b + c * 8 * EB;
+      const int j = (int)bi - pg_first;
+      const int32_t page = j < C::MAXPG ? pg[j] : bt_row[bi];
+      const int64_t off = (int64_t)page * blk_b + (int64_t)slot * slot_b + c * 8 * EB;
       if constexpr (FP8) {
         const u32x2 a = *reinterpret_cast<const u32x2*>(kbase + off);
         const u32x2 b = *reinterpret_cast<const u32x2*>(vbase + off);
@@ -118,8 +132,8 @@ __device__ __forceinline__ void stage_store(const Stage<QT, FP8, D>& st, uint16_
       a = u32x4{st.k[u][0], st.k[u][1], st.k[u][2], st.k[u][3]};
       b = u32x4{st.v[u][0], st.v[u][1], st.v[u][2], st.v[u][3]};
     }
-    *reinterpret_cast<u32x4*>(sk + swz<D>(key, c)) = a;
-    *reinterpret_cast<u32x4*>(sv + swz<D>(key, c)) = b;
+    *reinterpret_cast<u32x4*>(sk + lds_off<D>(key, c)) = a;
+    *reinterpret_cast<u32x4*>(sv + lds_off<D>(key, c)) = b;
   }
 }
 
@@ -131,7 +145,8 @@ __global__ __launch_bounds__(256, (D > 128 ? 1 : 2)) void large_kernel(Params p)
   __shared__ __attribute__((aligned(16))) uint16_t sV[2][C::TILE];
 
   const int tid = threadIdx.x;
-  const int lane = tid & 63, wave = tid >> 6;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int l32 = lane & 31, g2 = lane >> 5;
 
   // XCD-aware order: consecutive logical blocks (the query blocks of one kv
@@ -145,9 +160,16 @@ __global__ __launch_bounds__(256, (D > 128 ? 1 : 2)) void large_kernel(Params p)
   const int kvh = (lin / gx) % gy;
   const int part = lin / (gx * gy);
 
-  const int s = find_seq(p.cu_seqlens_q, p.num_seqs, qb, p.block_q);
+  int s, tok0;
+  if (p.seq_blocks) {
+    s = qb;
+    tok0 = p.cu_seqlens_q[s];
+  } else {
+    s = find_seq(p.cu_seqlens_q, p.num_seqs, qb, p.block_q);
+    const int qs = p.cu_seqlens_q[s];
+    tok0 = qs + (qb - (qs / p.block_q + s)) * p.block_q;
+  }
   const int q_start = p.cu_seqlens_q[s], q_end = p.cu_seqlens_q[s + 1];
-  const int tok0 = q_start + (qb - (q_start / p.block_q + s)) * p.block_q;
   if (tok0 >= q_end) return;
   const int ntok = min(p.block_q, q_end - tok0);
   const int kv_len = p.seq_lens[s];
@@ -218,16 +240,26 @@ __global__ __launch_bounds__(256, (D > 128 ? 1 : 2)) void large_kernel(Params p)
   float m_run = -INFINITY, l_run = 0.0f;
   const float c2 = p.qk_scale2;
 
+  // Stage the block-table entries of the workgroup's key range [kl, k1).
+  __shared__ int32_t sm_pg[C::MAXPG];
+  const int pg_first = (int)fastdiv((uint32_t)kl, p.bs_div);
+  {
+    const int npg = min((int)fastdiv((uint32_t)(k1 - 1), p.bs_div) - pg_first + 1, C::MAXPG);
+    for (int j = tid; j < npg; j += 256) sm_pg[j] = bt_row[pg_first + j];
+  }
+  __syncthreads();
+
   const int ntiles = (k1 - k0 + TK - 1) / TK;
   Stage<QT, FP8, D> st;
-  stage_load<QT, FP8, D>(st, p, bt_row, kbase, vbase, k0, kl, k1, tid);
+  stage_load<QT, FP8, D>(st, p, bt_row, sm_pg, pg_first, kbase, vbase, k0, kl, k1, tid);
   stage_store<QT, FP8, D>(st, sK[0], sV[0], tid);
   __syncthreads();
 
   for (int t = 0; t < ntiles; ++t) {
     const int kt = k0 + t * TK;
     const int buf = t & 1;
-    if (t + 1 < ntiles) stage_load<QT, FP8, D>(st, p, bt_row, kbase, vbase, kt + TK, kl, k1, tid);
+    if (t + 1 < ntiles)
+      stage_load<QT, FP8, D>(st, p, bt_row, sm_pg, pg_first, kbase, vbase, kt + TK, kl, k1, tid);
 
     if (wave_live) {
       const uint16_t* sk = sK[buf];
@@ -240,23 +272,18 @@ __global__ __launch_bounds__(256, (D > 128 ? 1 : 2)) void large_kernel(Params p)
         const int key = 32 * kb + l32;
 #pragma unroll
         for (int c = 0; c < C::QC; ++c) {
-          const u32x4 a = *reinterpret_cast<const u32x4*>(sk + swz<D>(key, 2 * c + g2));
+          const u32x4 a = *reinterpret_cast<const u32x4*>(sk + lds_off<D>(key, 2 * c + g2));
           sacc[kb] = mfma32<QT>(a, qop[c], sacc[kb]);
         }
       }
-      // ---- logits (base 2) and masks
-      const bool full = !general && kt >= kl && kt + TK <= k1 && kt + TK - 1 <= wave_pmin &&
+      // ---- logits and masks.  Without softcap/ALiBi the raw dot products are
+      // kept (cs = scale * log2 e is applied in the FMA feeding exp2); with them
+      // the base-2 logits are formed here (cs = 1).
+      const bool full = kt >= kl && kt + TK <= k1 && kt + TK - 1 <= wave_pmin &&
                         (p.window <= 0 || kt > wave_pmax - p.window);
-      float mt = -INFINITY;
-      if (full) {
-#pragma unroll
-        for (int kb = 0; kb < C::KB; ++kb)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            sacc[kb][r] *= c2;
-            mt = fmaxf(mt, sacc[kb][r]);
-          }
-      } else {
+      float cs = c2;
+      if (general) {
+        cs = 1.0f;
 #pragma unroll
         for (int kb = 0; kb < C::KB; ++kb)
 #pragma unroll
@@ -265,13 +292,25 @@ __global__ __launch_bounds__(256, (D > 128 ? 1 : 2)) void large_kernel(Params p)
             const float raw = sacc[kb][r];
             float v = p.softcap_on ? p.cap_out2 * tanh_fast(raw * p.cap_in) : raw * c2;
             v += slope2 * (float)(key - ctx);
-            v = (key >= row_lo && key < row_hi) ? v : -INFINITY;
-            sacc[kb][r] = v;
-            mt = fmaxf(mt, v);
+            sacc[kb][r] = (key >= row_lo && key < row_hi) ? v : -INFINITY;
+          }
+      } else if (!full) {
+#pragma unroll
+        for (int kb = 0; kb < C::KB; ++kb)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int key = kt + 32 * kb + 8 * (r >> 2) + 4 * g2 + (r & 3);
+            sacc[kb][r] = (key >= row_lo && key < row_hi) ? sacc[kb][r] : -INFINITY;
           }
       }
-      // Row maximum across the lane pair (l, l ^ 32) holding the same row.
-      mt = wave_max_xor(mt, 32);
+      float mt = -INFINITY;
+#pragma unroll
+      for (int kb = 0; kb < C::KB; ++kb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) mt = fmaxf(mt, sacc[kb][r]);
+      // Row maximum across the lane pair (l, l ^ 32) holding the same row,
+      // in base-2 logit units (cs > 0, and -inf stays -inf).
+      mt = wave_max_xor(mt, 32) * cs;
       // Move the running maximum only when this tile exceeds it by > 8 (base 2).
       const bool need = mt > m_run + 8.0f;
       if (__builtin_amdgcn_ballot_w64(need)) {
@@ -283,15 +322,16 @@ __global__ __launch_bounds__(256, (D > 128 ? 1 : 2)) void large_kernel(Params p)
         m_run = m_new;
       }
       const float m_use = (m_run == -INFINITY) ? 0.0f : m_run;
-      // ---- P = 2^(x - m), packed as the B operands of the PV MFMAs
+      // ---- P = 2^(s * cs - m), packed as the B operands of the PV MFMAs
       u32x4 pop[TK / 16];
       float psum = 0.0f;
 #pragma unroll
       for (int kk = 0; kk < TK / 16; ++kk) {
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
-          const float a = fast_exp2(sacc[kk >> 1][8 * (kk & 1) + 2 * q] - m_use);
-          const float b = fast_exp2(sacc[kk >> 1][8 * (kk & 1) + 2 * q + 1] - m_use);
+          const float a = fast_exp2(__builtin_fmaf(sacc[kk >> 1][8 * (kk & 1) + 2 * q], cs, -m_use));
+          const float b =
+              fast_exp2(__builtin_fmaf(sacc[kk >> 1][8 * (kk & 1) + 2 * q + 1], cs, -m_use));
           psum += a + b;
           pop[kk][q] = pack2<QT>(a, b);
         }
@@ -305,8 +345,8 @@ __global__ __launch_bounds__(256, (D > 128 ? 1 : 2)) void large_kernel(Params p)
 #pragma unroll
         for (int kk = 0; kk < TK / 16; ++kk) {
           const int key0 = 16 * kk + 4 * g2 + (s16 >> 2);
-          const u32x2 lo2 = lds_read_tr16(sv + swz<D>(key0, dcol >> 3) + (dcol & 7));
-          const u32x2 hi2 = lds_read_tr16(sv + swz<D>(key0 + 8, dcol >> 3) + (dcol & 7));
+          const u32x2 lo2 = lds_read_tr16(sv + key0 * C::PITCH + dcol);
+          const u32x2 hi2 = lds_read_tr16(sv + (key0 + 8) * C::PITCH + dcol);
           oacc[d] = mfma32<QT>(u32x4{lo2[0], lo2[1], hi2[0], hi2[1]}, pop[kk], oacc[d]);
         }
       }

@@ -12,15 +12,15 @@
 namespace ua {
 namespace {
 
-// One 64-thread workgroup per (row group): TPR threads own 4 head-dim values
-// of a row each.  All partition states are fetched before any is used (no
-// data-dependent branch between loads), so a row costs about two memory
-// round trips whatever the partition count.
+// One 64-thread workgroup per row group: TPR threads own 4 head-dim values of
+// a row each.  Partition states are fetched U at a time with every load of a
+// batch issued before any is used, and merged online (running maximum), so
+// up to U partitions cost one memory round trip.
 template <int OT, int D>
 __global__ __launch_bounds__(64) void reduce_kernel(Params p) {
   constexpr int TPR = D / 4;          // threads per row, 4 values each
   constexpr int RPB = 64 / TPR;       // rows per workgroup
-  constexpr int U = 8;                // partitions fetched per batch
+  constexpr int U = 16;               // partitions fetched per batch
   const int R = p.total_q * p.num_q_heads;
   const int tid = threadIdx.x;
   const int64_t row = (int64_t)blockIdx.x * RPB + tid / TPR;
@@ -29,22 +29,7 @@ __global__ __launch_bounds__(64) void reduce_kernel(Params p) {
   const int h = (int)(row % p.num_q_heads);
   const int P = p.n_part;
 
-  float M = -INFINITY;
-  for (int q0 = 0; q0 < P; q0 += U) {
-    float mv[U], lv[U];
-#pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const int q = q0 + u;
-      mv[u] = q < P ? p.ws_m[(int64_t)q * R + row] : -INFINITY;
-      lv[u] = q < P ? p.ws_l[(int64_t)q * R + row] : 0.0f;
-    }
-#pragma unroll
-    for (int u = 0; u < U; ++u) M = lv[u] > 0.0f ? fmaxf(M, mv[u]) : M;
-  }
-  const float sink2 = (p.sinks != nullptr) ? p.sinks[h] * kLog2e : -INFINITY;
-  const float Mt = fmaxf(M, sink2);
-  const float Ms = (Mt == -INFINITY) ? 0.0f : Mt;
-  float L = 0.0f;
+  float M = -INFINITY, L = 0.0f;
   f32x4 acc = {0.f, 0.f, 0.f, 0.f};
   for (int q0 = 0; q0 < P; q0 += U) {
     float mv[U], lv[U];
@@ -52,23 +37,37 @@ __global__ __launch_bounds__(64) void reduce_kernel(Params p) {
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       const int q = q0 + u;
-      mv[u] = q < P ? p.ws_m[(int64_t)q * R + row] : 0.0f;
-      lv[u] = q < P ? p.ws_l[(int64_t)q * R + row] : 0.0f;
-      av[u] = q < P ? *reinterpret_cast<const f32x4*>(p.ws_acc + ((int64_t)q * R + row) * D + d0)
-                    : f32x4{0.f, 0.f, 0.f, 0.f};
+      const bool in = q < P;
+      mv[u] = in ? p.ws_m[(int64_t)q * R + row] : -INFINITY;
+      lv[u] = in ? p.ws_l[(int64_t)q * R + row] : 0.0f;
+      av[u] = in ? *reinterpret_cast<const f32x4*>(p.ws_acc + ((int64_t)q * R + row) * D + d0)
+                 : f32x4{0.f, 0.f, 0.f, 0.f};
     }
+    float mb = M;
+#pragma unroll
+    for (int u = 0; u < U; ++u) mb = lv[u] > 0.0f ? fmaxf(mb, mv[u]) : mb;
+    if (mb == -INFINITY) continue;  // nothing live yet
+    const float f = fast_exp2(M - mb);  // M = -inf -> 0 (L and acc are 0 then)
+    L *= f;
+    acc *= f;
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       const bool live = lv[u] > 0.0f;  // l == 0: acc and m are unspecified, never used
-      const float w = live ? fast_exp2(mv[u] - Ms) : 0.0f;
+      const float w = live ? fast_exp2(mv[u] - mb) : 0.0f;
       L += w * lv[u];
 #pragma unroll
       for (int e = 0; e < 4; ++e) acc[e] += live ? w * av[u][e] : 0.0f;
     }
+    M = mb;
   }
   const bool any_key = L > 0.0f;
+  const float sink2 = (p.sinks != nullptr) ? p.sinks[h] * kLog2e : -INFINITY;
+  const float Mt = fmaxf(M, sink2);
+  const float Ms = (Mt == -INFINITY) ? 0.0f : Mt;
+  const float f = any_key ? fast_exp2(M - Ms) : 0.0f;
+  L *= f;
   if (sink2 != -INFINITY) L += fast_exp2(sink2 - Ms);
-  const float inv = any_key ? p.v_scale / L : 0.0f;
+  const float inv = any_key ? p.v_scale * f / L : 0.0f;
   const int64_t tok = row / p.num_q_heads;
   char* dst = reinterpret_cast<char*>(p.out) +
               (tok * p.o_stride_tok + (int64_t)h * p.o_stride_head + d0) * 2;

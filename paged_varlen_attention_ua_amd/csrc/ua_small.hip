@@ -13,14 +13,18 @@
 //
 // Data flow per 32-key tile and wave (no LDS in the loop):
 //   * K rows go straight from HBM into registers already in the MFMA A-operand
-//     layout (lane l: key l % 16, a contiguous quarter of the head dim), and
-//     S^T = K Q^T comes out with one query row per lane (row = l % 16).
+//     layout (lane l: key l % 16), and S^T = K Q^T comes out with one query row
+//     per lane (row = l % 16).
 //   * Because P^T then sits in the B-operand layout of O^T = V^T P^T, P stays
 //     in registers; the eight keys a lane contributes are the ones its S^T
 //     accumulator holds.
 //   * V is loaded as whole 16-byte row pieces (four full rows per load
 //     instruction) and the per-lane transposition the A operand needs is done
 //     with byte permutes in registers.
+//   * When block_size is a multiple of 16 each 16-key half tile lies in one
+//     cache block; the block-table entries of all of a wave's tiles are fetched
+//     in one lane-parallel load up front, so a tile's K/V loads never wait on a
+//     block-table load of their own.
 //   * Logits are kept in the base-2 domain (pre-multiplied by log2 e, exp2 for
 //     the exponentials), the README's convention (section "2D vs 2D").
 
@@ -60,6 +64,16 @@ struct SmallCfg {
   static constexpr int VW = E * EB / 4 > 0 ? E * EB / 4 : 1;  // dwords per lane per V row
 };
 
+// Head-dim index of element 0 of the c-th QK operand held by lane group g
+// (K and Q use the same map, so the contraction covers every index once).
+// 16-bit K: each load instruction covers 64 contiguous bytes of a row
+// (d = 32c + 8g + j); fp8 K: each lane owns one contiguous quarter of the
+// row (d = D/4 * g + 8c + j).
+template <bool FP8, int D>
+__device__ __forceinline__ int kq_index(int c, int g) {
+  return FP8 ? (D / 4) * g + 8 * c : 32 * c + 8 * g;
+}
+
 template <int QT, bool FP8, int D>
 struct Tile {
   using C = SmallCfg<QT, FP8, D>;
@@ -67,76 +81,98 @@ struct Tile {
   uint32_t v[8][C::VW];
 };
 
-template <int QT, bool FP8, int D, bool PAGE16>
-__device__ __forceinline__ void load_tile(Tile<QT, FP8, D>& t, const Params& p,
-                                          const int32_t* __restrict__ bt_row,
-                                          const char* kbase, const char* vbase, int kt, int kl,
-                                          int k1, int g, int r16) {
+// K row piece of one lane (`row` = byte address of the key's head row).
+template <int QT, bool FP8, int D>
+__device__ __forceinline__ void load_k_row(const char* row, int g, uint32_t* dst) {
+  using C = SmallCfg<QT, FP8, D>;
+  if constexpr (FP8) {
+    load_dw<C::KW>(row + kq_index<FP8, D>(0, g), dst);
+  } else {
+#pragma unroll
+    for (int c = 0; c < C::QC; ++c) load_dw<4>(row + 2 * kq_index<FP8, D>(c, g), dst + 4 * c);
+  }
+}
+
+// Tile loader for block_size % 16 == 0: `page[hb]` is the cache block of half
+// hb (wave-uniform; -1 when the half has no loadable key).  Loads are
+// unconditional: a lane whose key lies outside the tile's loadable range
+// [max(kl, kt), min(k1, kt + 32)) reads the nearest loadable key instead (a
+// real row of the same sequence, so finite), and the logit mask, which uses
+// the true key index, gives it zero weight.  Every issued tile has at least
+// one loadable key.
+template <int QT, bool FP8, int D>
+__device__ __forceinline__ void load_tile_paged16(Tile<QT, FP8, D>& t, const Params& p,
+                                                  const char* kbase, const char* vbase, int kt,
+                                                  const int32_t* page, int kl, int k1, int g,
+                                                  int r16) {
+  using C = SmallCfg<QT, FP8, D>;
+  const int64_t slot_b = p.kv_stride_slot * C::EB;
+  const int64_t blk_b = p.kv_stride_block * C::EB;
+  const int klo = max(kl, kt), khi = min(k1, kt + 32) - 1;
+  // Byte offset of the (page, slot) holding loadable key k of this tile.
+  int64_t hoff[2];
+#pragma unroll
+  for (int hb = 0; hb < 2; ++hb) {
+    const int kb0 = kt + 16 * hb;
+    const uint32_t bi = fastdiv((uint32_t)kb0, p.bs_div);
+    const int slot0 = kb0 - (int)bi * p.block_size;
+    hoff[hb] = (int64_t)page[hb] * blk_b + (int64_t)(slot0 - kb0) * slot_b;
+  }
+  auto key_off = [&](int key) -> int64_t {
+    const int kc = min(max(key, klo), khi);
+    return (kc - kt < 16 ? hoff[0] : hoff[1]) + (int64_t)kc * slot_b;
+  };
+#pragma unroll
+  for (int hb = 0; hb < 2; ++hb) {
+    load_k_row<QT, FP8, D>(kbase + key_off(kt + 16 * hb + r16), g, t.k[hb]);
+#pragma unroll
+    for (int jj = 0; jj < 4; ++jj)
+      load_dw<C::VW>(vbase + key_off(kt + 16 * hb + 4 * g + jj) + C::E * r16 * C::EB,
+                     t.v[4 * hb + jj]);
+  }
+}
+
+// Tile loader for any block size: one block-table lookup per key and lane.
+template <int QT, bool FP8, int D>
+__device__ __forceinline__ void load_tile_any(Tile<QT, FP8, D>& t, const Params& p,
+                                              const int32_t* __restrict__ bt_row,
+                                              const char* kbase, const char* vbase, int kt,
+                                              int kl, int k1, int g, int r16) {
   using C = SmallCfg<QT, FP8, D>;
   const int64_t slot_b = p.kv_stride_slot * C::EB;
   const int64_t blk_b = p.kv_stride_block * C::EB;
 #pragma unroll
   for (int hb = 0; hb < 2; ++hb) {
     const int kb0 = kt + 16 * hb;
-    if constexpr (PAGE16) {
-      // block_size % 16 == 0: the 16 keys of this half share one cache block.
-      const bool live = (kb0 < k1) && (kb0 + 16 > kl);
-      int64_t off = 0;
-      if (live) {
-        const uint32_t bi = fastdiv((uint32_t)kb0, p.bs_div);
-        const int slot0 = kb0 - (int)bi * p.block_size;
-        off = (int64_t)bt_row[bi] * blk_b + (int64_t)slot0 * slot_b;
+    {
+      const int key = kb0 + r16;
+      if (key >= kl && key < k1) {
+        const uint32_t bi = fastdiv((uint32_t)key, p.bs_div);
+        const int slot = key - (int)bi * p.block_size;
+        const int64_t off = (int64_t)bt_row[bi] * blk_b + (int64_t)slot * slot_b;
+        load_k_row<QT, FP8, D>(kbase + off, g, t.k[hb]);
+      } else {
+#pragma unroll
+        for (int i = 0; i < C::KW; ++i) t.k[hb][i] = 0;
       }
-      {
-        const int key = kb0 + r16;
-        if (live && key >= kl && key < k1)
-          load_dw<C::KW>(kbase + off + r16 * slot_b + C::DQ * g * C::EB, t.k[hb]);
-        else
+    }
 #pragma unroll
-          for (int i = 0; i < C::KW; ++i) t.k[hb][i] = 0;
-      }
+    for (int jj = 0; jj < 4; ++jj) {
+      const int key = kb0 + 4 * g + jj;
+      if (key >= kl && key < k1) {
+        const uint32_t bi = fastdiv((uint32_t)key, p.bs_div);
+        const int slot = key - (int)bi * p.block_size;
+        const int64_t off = (int64_t)bt_row[bi] * blk_b + (int64_t)slot * slot_b;
+        load_dw<C::VW>(vbase + off + C::E * r16 * C::EB, t.v[4 * hb + jj]);
+      } else {
 #pragma unroll
-      for (int jj = 0; jj < 4; ++jj) {
-        const int key = kb0 + 4 * g + jj;
-        if (live && key >= kl && key < k1)
-          load_dw<C::VW>(vbase + off + (4 * g + jj) * slot_b + C::E * r16 * C::EB,
-                         t.v[4 * hb + jj]);
-        else
-#pragma unroll
-          for (int i = 0; i < C::VW; ++i) t.v[4 * hb + jj][i] = 0;
-      }
-    } else {
-      {
-        const int key = kb0 + r16;
-        if (key >= kl && key < k1) {
-          const uint32_t bi = fastdiv((uint32_t)key, p.bs_div);
-          const int slot = key - (int)bi * p.block_size;
-          const int64_t off = (int64_t)bt_row[bi] * blk_b + (int64_t)slot * slot_b;
-          load_dw<C::KW>(kbase + off + C::DQ * g * C::EB, t.k[hb]);
-        } else {
-#pragma unroll
-          for (int i = 0; i < C::KW; ++i) t.k[hb][i] = 0;
-        }
-      }
-#pragma unroll
-      for (int jj = 0; jj < 4; ++jj) {
-        const int key = kb0 + 4 * g + jj;
-        if (key >= kl && key < k1) {
-          const uint32_t bi = fastdiv((uint32_t)key, p.bs_div);
-          const int slot = key - (int)bi * p.block_size;
-          const int64_t off = (int64_t)bt_row[bi] * blk_b + (int64_t)slot * slot_b;
-          load_dw<C::VW>(vbase + off + C::E * r16 * C::EB, t.v[4 * hb + jj]);
-        } else {
-#pragma unroll
-          for (int i = 0; i < C::VW; ++i) t.v[4 * hb + jj][i] = 0;
-        }
+        for (int i = 0; i < C::VW; ++i) t.v[4 * hb + jj][i] = 0;
       }
     }
   }
 }
 
-// A operand of the c-th QK MFMA for key half hb: 8 head-dim values of the
-// lane's K row (head-dim index D/4 * g + 8 c + j, matching the Q operand).
+// A operand of the c-th QK MFMA for key half hb.
 template <int QT, bool FP8, int D>
 __device__ __forceinline__ u32x4 k_operand(const Tile<QT, FP8, D>& t, int hb, int c) {
   if constexpr (FP8) {
@@ -170,19 +206,28 @@ __device__ __forceinline__ u32x4 v_operand(const Tile<QT, FP8, D>& t, int c) {
 }
 
 template <int QT, bool FP8, int D, bool SPLIT, bool PAGE16>
-__global__ __launch_bounds__(256, 2) void small_kernel(Params p) {
+__global__ __launch_bounds__(64 * kSmallWaves, (D > 128 ? 2 : 3)) void small_kernel(Params p) {
   using C = SmallCfg<QT, FP8, D>;
   constexpr int E = C::E;
   constexpr int QC = C::QC;
   constexpr int DQ = C::DQ;
+  constexpr int kStride = kSmallTile * kSmallWaves;
   const int tid = threadIdx.x;
-  const int lane = tid & 63, wave = tid >> 6;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int g = lane >> 4, r16 = lane & 15;
   const int qb = blockIdx.x, kvh = blockIdx.y, part = blockIdx.z;
 
-  const int s = find_seq(p.cu_seqlens_q, p.num_seqs, qb, p.block_q);
+  int s, tok0;
+  if (p.seq_blocks) {
+    s = qb;
+    tok0 = p.cu_seqlens_q[s];
+  } else {
+    s = find_seq(p.cu_seqlens_q, p.num_seqs, qb, p.block_q);
+    const int qs = p.cu_seqlens_q[s];
+    tok0 = qs + (qb - (qs / p.block_q + s)) * p.block_q;
+  }
   const int q_start = p.cu_seqlens_q[s], q_end = p.cu_seqlens_q[s + 1];
-  const int tok0 = q_start + (qb - (q_start / p.block_q + s)) * p.block_q;
   if (tok0 >= q_end) return;
   const int ntok = min(p.block_q, q_end - tok0);
   const int kv_len = p.seq_lens[s];
@@ -217,6 +262,27 @@ __global__ __launch_bounds__(256, 2) void small_kernel(Params p) {
     return;
   }
 
+  // This wave's tiles: kt = wk0 + kStride * i, i < nt.
+  const int wk0 = k0 + kSmallTile * wave;
+  const int nt = wk0 < k1 ? (k1 - wk0 + kStride - 1) / kStride : 0;
+  const int32_t* bt_row = p.block_table + (int64_t)s * p.max_blocks_per_seq;
+
+  // Block-table entries of this wave's first kPreTiles tiles, staged in the
+  // wave's own LDS slice: entry 2i + hb is the block of tile i, half hb (-1 when
+  // the half has no loadable key).  Reading them later waits only on LDS, never
+  // on the tile loads in flight.
+  constexpr int kPreTiles = 256;
+  __shared__ int32_t sm_pg[kSmallWaves][2 * kPreTiles];
+  auto entry = [&](int j) -> int32_t {
+    const int i = j >> 1;
+    const int kb0 = wk0 + kStride * i + 16 * (j & 1);
+    return (kb0 < k1 && kb0 + 16 > kl) ? bt_row[fastdiv((uint32_t)kb0, p.bs_div)] : -1;
+  };
+  if constexpr (PAGE16) {
+    const int ne = 2 * min(nt, kPreTiles);
+    for (int j = lane; j < ne; j += 64) sm_pg[wave][j] = entry(j);
+  }
+
   // This lane's query row.
   const int rt = r16 / G, rh = r16 - rt * G;
   const bool row_ok = (r16 < p.block_q * G) && (rt < ntok);
@@ -226,29 +292,46 @@ __global__ __launch_bounds__(256, 2) void small_kernel(Params p) {
   const int row_hi = min(k1, pos + 1);
   const float slope2 = (p.alibi != nullptr && row_ok) ? p.alibi[h] * kLog2e : 0.0f;
 
-  // Q as the B operand of S^T = K Q^T: lane holds head-dim values [DQ*g, DQ*g + DQ).
+  // Q as the B operand of S^T = K Q^T (same head-dim map as K).
   u32x4 qop[QC];
   if (row_ok) {
     const char* qp = reinterpret_cast<const char*>(p.q) +
-                     ((int64_t)(tok0 + rt) * p.q_stride_tok + (int64_t)h * p.q_stride_head +
-                      DQ * g) * 2;
+                     ((int64_t)(tok0 + rt) * p.q_stride_tok + (int64_t)h * p.q_stride_head) * 2;
 #pragma unroll
-    for (int c = 0; c < QC; ++c) qop[c] = *reinterpret_cast<const u32x4*>(qp + 16 * c);
+    for (int c = 0; c < QC; ++c)
+      qop[c] = *reinterpret_cast<const u32x4*>(qp + 2 * kq_index<FP8, D>(c, g));
   } else {
 #pragma unroll
     for (int c = 0; c < QC; ++c) qop[c] = u32x4{0, 0, 0, 0};
   }
 
-  const int32_t* bt_row = p.block_table + (int64_t)s * p.max_blocks_per_seq;
   const char* kbase = reinterpret_cast<const char*>(p.k) + kvh * p.kv_stride_head * C::EB;
   const char* vbase = reinterpret_cast<const char*>(p.v) + kvh * p.kv_stride_head * C::EB;
+
+  auto load = [&](Tile<QT, FP8, D>& t, int i) {
+    const int kt = wk0 + kStride * i;
+    if constexpr (PAGE16) {
+      int32_t page[2];
+      if (i < kPreTiles) {
+        page[0] = __builtin_amdgcn_readfirstlane(sm_pg[wave][2 * i]);
+        page[1] = __builtin_amdgcn_readfirstlane(sm_pg[wave][2 * i + 1]);
+      } else {
+        page[0] = entry(2 * i);
+        page[1] = entry(2 * i + 1);
+      }
+      load_tile_paged16<QT, FP8, D>(t, p, kbase, vbase, kt, page, kl, k1, g, r16);
+    } else {
+      load_tile_any<QT, FP8, D>(t, p, bt_row, kbase, vbase, kt, kl, k1, g, r16);
+    }
+  };
 
   f32x4 oacc[E];
 #pragma unroll
   for (int c = 0; c < E; ++c) oacc[c] = f32x4{0.f, 0.f, 0.f, 0.f};
   float m_run = -INFINITY, l_run = 0.0f;
 
-  auto compute = [&](const Tile<QT, FP8, D>& t, int kt) {
+  auto compute = [&](const Tile<QT, FP8, D>& t, int i) {
+    const int kt = wk0 + kStride * i;
     f32x4 sacc[2];
 #pragma unroll
     for (int hb = 0; hb < 2; ++hb) {
@@ -292,36 +375,70 @@ __global__ __launch_bounds__(256, 2) void small_kernel(Params p) {
     for (int c = 0; c < E; ++c) oacc[c] = mfma16<QT>(v_operand(t, c), pb, oacc[c]);
   };
 
-  // Two-stage register pipeline: the next tile's loads are in flight while
-  // the current tile is computed.
-  int kt = k0 + kSmallTile * wave;
-  constexpr int kStride = kSmallTile * kSmallWaves;
-  if constexpr (D > 128) {
-    // A 256-wide tile is 128 registers per lane: no second stage.
-    for (; kt < k1; kt += kStride) {
-      Tile<QT, FP8, D> t1;
-      load_tile<QT, FP8, D, PAGE16>(t1, p, bt_row, kbase, vbase, kt, kl, k1, g, r16);
-      compute(t1, kt);
-    }
-  } else {
-  Tile<QT, FP8, D> ta, tb;
-  if (kt < k1) load_tile<QT, FP8, D, PAGE16>(ta, p, bt_row, kbase, vbase, kt, kl, k1, g, r16);
-  while (kt < k1) {
-    if (kt + kStride < k1)
-      load_tile<QT, FP8, D, PAGE16>(tb, p, bt_row, kbase, vbase, kt + kStride, kl, k1, g, r16);
-    compute(ta, kt);
-    kt += kStride;
-    if (kt >= k1) break;
-    if (kt + kStride < k1)
-      load_tile<QT, FP8, D, PAGE16>(ta, p, bt_row, kbase, vbase, kt + kStride, kl, k1, g, r16);
-    compute(tb, kt);
-    kt += kStride;
-  }
+  // One tile per wave in flight; latency is hidden by running three waves per
+  // SIMD (measured faster on MI355X than a two-tile register pipeline, whose
+  // register pressure made the allocator reuse registers with loads in flight).
+  for (int i = 0; i < nt; ++i) {
+    Tile<QT, FP8, D> t1;
+    load(t1, i);
+    compute(t1, i);
   }
 
-  // Merge the four waves' states through LDS.
+  // Row state of this wave: m_run is already the row maximum across the four
+  // lanes holding a row; l needs their sum.
   float l_row = wave_sum_xor(l_run, 16);
   l_row = wave_sum_xor(l_row, 32);
+
+  if constexpr (kSmallWaves == 1) {
+    // One wave: write straight from registers.  O^T accumulator register
+    // (c, r) holds O[row l%16][D/4*g + E*r + c].
+    if (!row_ok) return;
+    const int tok = tok0 + rt;
+    const int64_t rrow = (int64_t)tok * p.num_q_heads + h;
+    if constexpr (SPLIT) {
+      if (g == 0) {
+        p.ws_m[(int64_t)part * R + rrow] = m_run;
+        p.ws_l[(int64_t)part * R + rrow] = l_row;
+      }
+      float* dst = p.ws_acc + ((int64_t)part * R + rrow) * D + DQ * g;
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+#pragma unroll
+        for (int c = 0; c < E; c += 4)
+          *reinterpret_cast<f32x4*>(dst + E * r + c) =
+              f32x4{oacc[c][r], oacc[c + 1][r], oacc[c + 2][r], oacc[c + 3][r]};
+    } else {
+      const float sink2 = p.sinks != nullptr ? p.sinks[h] * kLog2e : -INFINITY;
+      const float Mt = fmaxf(m_run, sink2);
+      const float Ms = (Mt == -INFINITY) ? 0.0f : Mt;
+      const float f = fast_exp2(m_run - Ms);
+      float L = l_row * f;
+      const bool any_key = L > 0.0f;
+      if (sink2 != -INFINITY) L += fast_exp2(sink2 - Ms);
+      const float inv = any_key ? p.v_scale * f / L : 0.0f;
+      char* dst = reinterpret_cast<char*>(p.out) +
+                  ((int64_t)tok * p.o_stride_tok + (int64_t)h * p.o_stride_head + DQ * g) * 2;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        uint32_t packed[E / 2];
+#pragma unroll
+        for (int c = 0; c < E; c += 2) packed[c / 2] = pack2<QT>(oacc[c][r] * inv, oacc[c + 1][r] * inv);
+        if constexpr (E == 8) {
+          *reinterpret_cast<u32x4*>(dst + 2 * E * r) = u32x4{packed[0], packed[1], packed[2], packed[3]};
+        } else if constexpr (E == 16) {
+          *reinterpret_cast<u32x4*>(dst + 2 * E * r) = u32x4{packed[0], packed[1], packed[2], packed[3]};
+          *reinterpret_cast<u32x4*>(dst + 2 * E * r + 16) =
+              u32x4{packed[4], packed[5], packed[6], packed[7]};
+        } else {
+          *reinterpret_cast<u32x2*>(dst + 2 * E * r) = u32x2{packed[0], packed[1]};
+        }
+      }
+      if (p.lse != nullptr && g == 0)
+        p.lse[rrow] = (L > 0.0f) ? (Ms + fast_log2(L)) * kLn2 : -INFINITY;
+    }
+    return;
+  } else {
+  // Several waves: merge their states through LDS.
   if (g == 0) {
     sm_m[wave][r16] = m_run;
     sm_l[wave][r16] = l_row;
@@ -333,64 +450,67 @@ __global__ __launch_bounds__(256, 2) void small_kernel(Params p) {
     for (int r = 0; r < 4; ++r) sm_o[wave][r16][DQ * g + E * r + c] = oacc[c][r];
   __syncthreads();
 
-  const int row = tid >> 4, chunk = tid & 15;
-  const int mrt = row / G, mrh = row - (row / G) * G;
-  if (!(row < p.block_q * G && mrt < ntok)) return;
-  const int tok = tok0 + mrt, hh = kvh * G + mrh;
-  float mw[kSmallWaves];
-  float M = -INFINITY;
+  for (int idx = tid; idx < 256; idx += 64 * kSmallWaves) {
+    const int row = idx >> 4, chunk = idx & 15;
+    const int mrt = row / G, mrh = row - (row / G) * G;
+    if (!(row < p.block_q * G && mrt < ntok)) continue;
+    const int tok = tok0 + mrt, hh = kvh * G + mrh;
+    float mw[kSmallWaves];
+    float M = -INFINITY;
 #pragma unroll
-  for (int w = 0; w < kSmallWaves; ++w) {
-    mw[w] = sm_m[w][row];
-    M = fmaxf(M, mw[w]);
-  }
-  const float sink2 = (!SPLIT && p.sinks != nullptr) ? p.sinks[hh] * kLog2e : -INFINITY;
-  const float Mt = fmaxf(M, sink2);
-  const float Ms = (Mt == -INFINITY) ? 0.0f : Mt;
-  float L = 0.0f;
-  float f[kSmallWaves];
-#pragma unroll
-  for (int w = 0; w < kSmallWaves; ++w) {
-    f[w] = fast_exp2(mw[w] - Ms);
-    L += f[w] * sm_l[w][row];
-  }
-  const bool any_key = L > 0.0f;
-  float o[E];
-#pragma unroll
-  for (int e = 0; e < E; ++e) {
-    float a = 0.0f;
-#pragma unroll
-    for (int w = 0; w < kSmallWaves; ++w) a += f[w] * sm_o[w][row][E * chunk + e];
-    o[e] = a;
-  }
-  const int64_t rrow = (int64_t)tok * p.num_q_heads + hh;
-  if constexpr (SPLIT) {
-    if (chunk == 0) {
-      p.ws_m[(int64_t)part * R + rrow] = M;
-      p.ws_l[(int64_t)part * R + rrow] = L;
+    for (int w = 0; w < kSmallWaves; ++w) {
+      mw[w] = sm_m[w][row];
+      M = fmaxf(M, mw[w]);
     }
-    float* dst = p.ws_acc + ((int64_t)part * R + rrow) * D + E * chunk;
+    const float sink2 = (!SPLIT && p.sinks != nullptr) ? p.sinks[hh] * kLog2e : -INFINITY;
+    const float Mt = fmaxf(M, sink2);
+    const float Ms = (Mt == -INFINITY) ? 0.0f : Mt;
+    float L = 0.0f;
+    float f[kSmallWaves];
 #pragma unroll
-    for (int e = 0; e < E; e += 4)
-      *reinterpret_cast<f32x4*>(dst + e) = f32x4{o[e], o[e + 1], o[e + 2], o[e + 3]};
-  } else {
-    if (sink2 != -INFINITY) L += fast_exp2(sink2 - Ms);
-    const float inv = any_key ? p.v_scale / L : 0.0f;
-    uint32_t packed[E / 2];
+    for (int w = 0; w < kSmallWaves; ++w) {
+      f[w] = fast_exp2(mw[w] - Ms);
+      L += f[w] * sm_l[w][row];
+    }
+    const bool any_key = L > 0.0f;
+    float o[E];
 #pragma unroll
-    for (int e = 0; e < E; e += 2) packed[e / 2] = pack2<QT>(o[e] * inv, o[e + 1] * inv);
-    char* dst = reinterpret_cast<char*>(p.out) +
-                ((int64_t)tok * p.o_stride_tok + (int64_t)hh * p.o_stride_head + E * chunk) * 2;
-    if constexpr (E == 8) {
-      *reinterpret_cast<u32x4*>(dst) = u32x4{packed[0], packed[1], packed[2], packed[3]};
-    } else if constexpr (E == 16) {
-      *reinterpret_cast<u32x4*>(dst) = u32x4{packed[0], packed[1], packed[2], packed[3]};
-      *reinterpret_cast<u32x4*>(dst + 16) = u32x4{packed[4], packed[5], packed[6], packed[7]};
+    for (int e = 0; e < E; ++e) {
+      float a = 0.0f;
+#pragma unroll
+      for (int w = 0; w < kSmallWaves; ++w) a += f[w] * sm_o[w][row][E * chunk + e];
+      o[e] = a;
+    }
+    const int64_t rrow = (int64_t)tok * p.num_q_heads + hh;
+    if constexpr (SPLIT) {
+      if (chunk == 0) {
+        p.ws_m[(int64_t)part * R + rrow] = M;
+        p.ws_l[(int64_t)part * R + rrow] = L;
+      }
+      float* dst = p.ws_acc + ((int64_t)part * R + rrow) * D + E * chunk;
+#pragma unroll
+      for (int e = 0; e < E; e += 4)
+        *reinterpret_cast<f32x4*>(dst + e) = f32x4{o[e], o[e + 1], o[e + 2], o[e + 3]};
     } else {
-      *reinterpret_cast<u32x2*>(dst) = u32x2{packed[0], packed[1]};
+      if (sink2 != -INFINITY) L += fast_exp2(sink2 - Ms);
+      const float inv = any_key ? p.v_scale / L : 0.0f;
+      uint32_t packed[E / 2];
+#pragma unroll
+      for (int e = 0; e < E; e += 2) packed[e / 2] = pack2<QT>(o[e] * inv, o[e + 1] * inv);
+      char* dst = reinterpret_cast<char*>(p.out) +
+                  ((int64_t)tok * p.o_stride_tok + (int64_t)hh * p.o_stride_head + E * chunk) * 2;
+      if constexpr (E == 8) {
+        *reinterpret_cast<u32x4*>(dst) = u32x4{packed[0], packed[1], packed[2], packed[3]};
+      } else if constexpr (E == 16) {
+        *reinterpret_cast<u32x4*>(dst) = u32x4{packed[0], packed[1], packed[2], packed[3]};
+        *reinterpret_cast<u32x4*>(dst + 16) = u32x4{packed[4], packed[5], packed[6], packed[7]};
+      } else {
+        *reinterpret_cast<u32x2*>(dst) = u32x2{packed[0], packed[1]};
+      }
+      if (p.lse != nullptr && chunk == 0)
+        p.lse[rrow] = (L > 0.0f) ? (Ms + fast_log2(L)) * kLn2 : -INFINITY;
     }
-    if (p.lse != nullptr && chunk == 0)
-      p.lse[rrow] = (L > 0.0f) ? (Ms + fast_log2(L)) * kLn2 : -INFINITY;
+  }
   }
 }
 
@@ -399,14 +519,14 @@ hipError_t launch_small_t(const Params& p, bool split, dim3 grid, hipStream_t st
   const bool page16 = (p.block_size % 16) == 0;
   if (split) {
     if (page16)
-      hipLaunchKernelGGL((small_kernel<QT, FP8, D, true, true>), grid, dim3(256), 0, stream, p);
+      hipLaunchKernelGGL((small_kernel<QT, FP8, D, true, true>), grid, dim3(64 * kSmallWaves), 0, stream, p);
     else
-      hipLaunchKernelGGL((small_kernel<QT, FP8, D, true, false>), grid, dim3(256), 0, stream, p);
+      hipLaunchKernelGGL((small_kernel<QT, FP8, D, true, false>), grid, dim3(64 * kSmallWaves), 0, stream, p);
   } else {
     if (page16)
-      hipLaunchKernelGGL((small_kernel<QT, FP8, D, false, true>), grid, dim3(256), 0, stream, p);
+      hipLaunchKernelGGL((small_kernel<QT, FP8, D, false, true>), grid, dim3(64 * kSmallWaves), 0, stream, p);
     else
-      hipLaunchKernelGGL((small_kernel<QT, FP8, D, false, false>), grid, dim3(256), 0, stream, p);
+      hipLaunchKernelGGL((small_kernel<QT, FP8, D, false, false>), grid, dim3(64 * kSmallWaves), 0, stream, p);
   }
   return hipGetLastError();
 }

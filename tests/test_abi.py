@@ -72,10 +72,12 @@ def status_of(p, force_path=0, n_part=0):
 def test_long_decode_splits_to_fill_the_device():
     st, plan = status_of(problem())
     assert st == 0 and plan.path == B.UA_PATH_SPLITKV
-    assert plan.n_part == 16  # 8 seqs x 8 kv heads = 64 groups, 4096-key window
-    assert plan.grid_y == 8 and plan.grid_z == 16
+    assert plan.n_part == 4  # 8 seqs x 8 kv heads = 64 groups: one workgroup per CU
+    assert plan.grid_y == 8 and plan.grid_z == 4 and plan.grid_x == 8  # one block per sequence
     R = 8 * 32
-    assert plan.workspace_bytes == ((2 * 16 * R * 4 + 255) & ~255) + 16 * R * 128 * 4
+    assert plan.workspace_bytes == ((2 * 4 * R * 4 + 255) & ~255) + 4 * R * 128 * 4
+    st, plan = status_of(problem(kv_dtype=B.UA_FP8_E4M3FN, kv_stride_block=16 * 8 * 128))
+    assert st == 0 and plan.n_part == 8
 
 
 def test_short_context_full_grid_stays_one_pass():
