@@ -4,12 +4,14 @@
 // block_q = 128 / G tokens times the G query heads of the kv head (grouped
 // rows share every K/V tile).  Four waves own 32 rows each.  Per 64-key tile
 // (32 keys for head dim 256):
-//   * the tile's K and V rows are gathered through the block table (its entries
-//     for the workgroup's key range are staged in LDS once) with 16-byte loads
-//     into registers, the next tile in flight while the current one is
-//     computed, and stored into double-buffered LDS rows padded to D + 16
-//     values (no bank conflicts for either read pattern below, and every read
-//     address is a per-lane base plus a constant);
+//   * the byte offsets of the tile's K/V rows are looked up through the block
+//     table one tile ahead (its entries for the workgroup's key range are
+//     staged in LDS once) by one wave, into a small LDS table;
+//   * the rows are copied HBM -> LDS with global_load_lds_dwordx4 (16-bit
+//     caches; no register staging) or through registers with the fp8 -> 16-bit
+//     conversion (fp8 caches), into double-buffered 256-byte-aligned rows whose
+//     16-byte slots are XOR-swizzled so that both read patterns below are
+//     free of LDS bank conflicts;
 //   * S^T = K Q^T on 32x32x16 MFMA (A = K from LDS, B = Q held in registers),
 //     so each lane owns one query row and 16 keys of each 32-key block;
 //   * online softmax in the base-2 domain (README section "2D vs 2D") on the
@@ -25,6 +27,8 @@
 //     ds_read_b64_tr_b16 transposed LDS reads (README "3D vs 3D").
 // Output: the final rows (one pass) or the partition's (m, l, acc) (split).
 
+#include <type_traits>
+
 #include "ua_device.h"
 
 namespace ua {
@@ -35,11 +39,11 @@ typedef short s16x4 __attribute__((ext_vector_type(4)));
 // Transposed LDS read: within each 16-lane group, lane s gives the address of
 // 4 consecutive 16-bit values of row s/4 (columns 4(s%4)..+3) of a 4 x 16
 // block; lane i receives column i of the 4 rows.
-__device__ __forceinline__ u32x2 lds_read_tr16(const uint16_t* p) {
+__device__ __forceinline__ u32x2 lds_read_tr16(const char* p) {
 #if defined(__HIP_DEVICE_COMPILE__)
   typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
   s16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-      (lds_s16x4*)((__attribute__((address_space(3))) uint16_t*)(p)));
+      (lds_s16x4*)((__attribute__((address_space(3))) char*)(p)));
   return __builtin_bit_cast(u32x2, v);
 #else
   (void)p;
@@ -47,102 +51,75 @@ __device__ __forceinline__ u32x2 lds_read_tr16(const uint16_t* p) {
 #endif
 }
 
+// Asynchronous 16-byte copy global -> LDS: lane i's 16 bytes land at
+// lds_uniform + 16 i (the LDS address is wave-uniform).  Completion is
+// tracked by vmcnt.
+__device__ __forceinline__ void load_lds16(const char* src, char* lds_uniform) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  __builtin_amdgcn_global_load_lds((const void*)src,
+                                   (__attribute__((address_space(3))) void*)lds_uniform, 16, 0,
+                                   0);
+#else
+  (void)src;
+  (void)lds_uniform;
+#endif
+}
+
+// Wait until every global load of this wave (including LDS copies) is done.
+__device__ __forceinline__ void wait_vmem() {
+  __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0), expcnt and lgkmcnt not waited on
+}
+
 template <int D>
 struct LargeCfg {
   static constexpr int TK = D > 128 ? 32 : 64;  // keys per tile
-  static constexpr int NC = D / 8;               // 16-byte chunks per K/V row
+  static constexpr int NC = D / 8;               // 16-byte slots per K/V row (16-bit values)
+  static constexpr int ROWB = 2 * D;             // LDS bytes per row
+  static constexpr int TILEB = TK * ROWB;        // LDS bytes per K (or V) tile buffer
+  static constexpr int BPW = TILEB / 1024 / 4;   // 1 KiB copy blocks per wave per buffer
   static constexpr int KB = TK / 32;             // 32-key blocks per tile
   static constexpr int QC = D / 16;              // QK MFMAs per 32-key block
   static constexpr int DB = D / 32;              // PV output blocks of 32 head-dim rows
-  static constexpr int PITCH = D + 16;           // LDS row pitch in 16-bit values
-  static constexpr int TILE = TK * PITCH;        // values per K (or V) tile buffer
-  static constexpr int CPT = TK * NC / 256;      // 16-byte chunks per thread per tile
+  static constexpr int CPT = TK * NC / 256;      // slots per thread per tile (fp8 staging)
   static constexpr int MAXPG = 1024;             // block-table entries staged in LDS
 };
 
-// Offset (in 16-bit values) of (key, 8-value chunk c) in a tile buffer.  With
-// a pitch of D + 16 values, consecutive rows start 32 bytes (8 banks) apart:
-// 8 keys reading the same 16-byte chunk, and 4 keys reading one 32-byte piece
-// (the transposed reads), touch disjoint banks.
+// Physical 16-byte slot of logical slot c in LDS row r is c ^ swz<D>(r).
+// gfx950 LDS serves 256 bytes (64 banks) per cycle: 16 lanes of a 16-byte
+// read, 32 lanes of an 8-byte read.  The K reads (16 consecutive rows, one
+// slot) need swz to be one-to-one on those rows' bank groups; the transposed
+// V reads (4 consecutive rows x 4 consecutive slots starting at a multiple of
+// 4) need the 16 (row, slot) pairs to land on 16 different bank groups.
+// D >= 128 (rows of >= 16 slots): swz(r) = 4 (r mod 4) + (r / 4) mod 4.
+// D = 64 (rows of 8 slots, two rows per 256 bytes): swz(r) = 4 ((r / 2) mod 2)
+// + (r / 4) mod 4.
 template <int D>
-__device__ __forceinline__ int lds_off(int key, int c) {
-  return key * LargeCfg<D>::PITCH + c * 8;
+__device__ __forceinline__ int swz(int r) {
+  if constexpr (D >= 128)
+    return ((r & 3) << 2) | ((r >> 2) & 3);
+  else
+    return (((r >> 1) & 1) << 2) | ((r >> 2) & 3);
 }
 
-template <int QT, bool FP8, int D>
+template <bool FP8, int D>
 struct Stage {
-  // FP8: 8 codes (2 dwords) per chunk; else 8 values (4 dwords) per chunk.
-  uint32_t k[LargeCfg<D>::CPT][FP8 ? 2 : 4];
-  uint32_t v[LargeCfg<D>::CPT][FP8 ? 2 : 4];
+  // fp8 staging only: 8 codes (2 dwords) per slot.
+  uint32_t k[FP8 ? LargeCfg<D>::CPT : 1][2];
+  uint32_t v[FP8 ? LargeCfg<D>::CPT : 1][2];
 };
-
-// Gather one tile's K/V chunks into registers.  `pg` holds the block-table
-// entries of blocks pg_first .. pg_first + MAXPG - 1 (the workgroup's range).
-template <int QT, bool FP8, int D>
-__device__ __forceinline__ void stage_load(Stage<QT, FP8, D>& st, const Params& p,
-                                           const int32_t* __restrict__ bt_row,
-                                           const int32_t* pg, int pg_first, const char* kbase,
-                                           const char* vbase, int kt, int kl, int k1, int tid) {
-  using C = LargeCfg<D>;
-  constexpr int EB = FP8 ? 1 : 2;
-  const int64_t slot_b = p.kv_stride_slot * EB;
-  const int64_t blk_b = p.kv_stride_block * EB;
-#pragma unroll
-  for (int u = 0; u < C::CPT; ++u) {
-    const int i = tid + 256 * u;
-    const int key = i / C::NC, c = i % C::NC;
-    const int kk = kt + key;
-    if (kk >= kl && kk < k1) {
-      const uint32_t bi = fastdiv((uint32_t)kk, p.bs_div);
-      const int slot = kk - (int)bi * p.block_size;
-      const int j = (int)bi - pg_first;
-      const int32_t page = j < C::MAXPG ? pg[j] : bt_row[bi];
-      const int64_t off = (int64_t)page * blk_b + (int64_t)slot * slot_b + c * 8 * EB;
-      if constexpr (FP8) {
-        const u32x2 a = *reinterpret_cast<const u32x2*>(kbase + off);
-        const u32x2 b = *reinterpret_cast<const u32x2*>(vbase + off);
-        st.k[u][0] = a[0]; st.k[u][1] = a[1];
-        st.v[u][0] = b[0]; st.v[u][1] = b[1];
-      } else {
-        const u32x4 a = *reinterpret_cast<const u32x4*>(kbase + off);
-        const u32x4 b = *reinterpret_cast<const u32x4*>(vbase + off);
-#pragma unroll
-        for (int w = 0; w < 4; ++w) { st.k[u][w] = a[w]; st.v[u][w] = b[w]; }
-      }
-    } else {
-#pragma unroll
-      for (int w = 0; w < (FP8 ? 2 : 4); ++w) { st.k[u][w] = 0; st.v[u][w] = 0; }
-    }
-  }
-}
-
-template <int QT, bool FP8, int D>
-__device__ __forceinline__ void stage_store(const Stage<QT, FP8, D>& st, uint16_t* sk,
-                                            uint16_t* sv, int tid) {
-  using C = LargeCfg<D>;
-#pragma unroll
-  for (int u = 0; u < C::CPT; ++u) {
-    const int i = tid + 256 * u;
-    const int key = i / C::NC, c = i % C::NC;
-    u32x4 a, b;
-    if constexpr (FP8) {
-      a = fp8x8_to<QT>(u32x2{st.k[u][0], st.k[u][1]});
-      b = fp8x8_to<QT>(u32x2{st.v[u][0], st.v[u][1]});
-    } else {
-      a = u32x4{st.k[u][0], st.k[u][1], st.k[u][2], st.k[u][3]};
-      b = u32x4{st.v[u][0], st.v[u][1], st.v[u][2], st.v[u][3]};
-    }
-    *reinterpret_cast<u32x4*>(sk + lds_off<D>(key, c)) = a;
-    *reinterpret_cast<u32x4*>(sv + lds_off<D>(key, c)) = b;
-  }
-}
 
 template <int QT, bool FP8, int D, bool SPLIT>
 __global__ __launch_bounds__(256, (D > 128 ? 1 : 2)) void large_kernel(Params p) {
   using C = LargeCfg<D>;
   constexpr int TK = C::TK;
-  __shared__ __attribute__((aligned(16))) uint16_t sK[2][C::TILE];
-  __shared__ __attribute__((aligned(16))) uint16_t sV[2][C::TILE];
+  constexpr int ROWB = C::ROWB;
+  __shared__ __attribute__((aligned(1024))) char sK0[C::TILEB];
+  __shared__ __attribute__((aligned(1024))) char sK1[C::TILEB];
+  __shared__ __attribute__((aligned(1024))) char sV0[C::TILEB];
+  __shared__ __attribute__((aligned(1024))) char sV1[C::TILEB];
+  __shared__ int64_t sTab0[TK];
+  __shared__ int64_t sTab1[TK];
+  __shared__ int32_t sm_pg[C::MAXPG];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -233,6 +210,8 @@ __global__ __launch_bounds__(256, (D > 128 ? 1 : 2)) void large_kernel(Params p)
   constexpr int EB = FP8 ? 1 : 2;
   const char* kbase = reinterpret_cast<const char*>(p.k) + kvh * p.kv_stride_head * EB;
   const char* vbase = reinterpret_cast<const char*>(p.v) + kvh * p.kv_stride_head * EB;
+  const int64_t slot_b = p.kv_stride_slot * EB;
+  const int64_t blk_b = p.kv_stride_block * EB;
 
   f32x16 oacc[C::DB];
 #pragma unroll
@@ -241,7 +220,6 @@ __global__ __launch_bounds__(256, (D > 128 ? 1 : 2)) void large_kernel(Params p)
   const float c2 = p.qk_scale2;
 
   // Stage the block-table entries of the workgroup's key range [kl, k1).
-  __shared__ int32_t sm_pg[C::MAXPG];
   const int pg_first = (int)fastdiv((uint32_t)kl, p.bs_div);
   {
     const int npg = min((int)fastdiv((uint32_t)(k1 - 1), p.bs_div) - pg_first + 1, C::MAXPG);
@@ -249,110 +227,249 @@ __global__ __launch_bounds__(256, (D > 128 ? 1 : 2)) void large_kernel(Params p)
   }
   __syncthreads();
 
+  // Row byte offsets (page * block stride + slot * slot stride) of keys
+  // kt .. kt + TK - 1, each clamped into [kl, k1 - 1]: a key outside the range
+  // reads a real row of the sequence (finite values) whose score is masked.
+  auto fill_tab = [&](int64_t* tab, int kt) __attribute__((always_inline)) {
+    if (lane < TK) {
+      const int key = min(max(kt + lane, kl), k1 - 1);
+      const uint32_t bi = fastdiv((uint32_t)key, p.bs_div);
+      const int slot = key - (int)bi * p.block_size;
+      const int j = (int)bi - pg_first;
+      const int32_t page = j < C::MAXPG ? sm_pg[j] : bt_row[bi];
+      tab[lane] = (int64_t)page * blk_b + (int64_t)slot * slot_b;
+    }
+  };
+
+  // 16-bit caches: copy block b = 4u + wave (1 KiB = 64 slots) of a tile;
+  // lane i fills physical slot n = 64 b + i, i.e. row n / NC, logical slot
+  // (n % NC) ^ swz(row).  swz reads bits 0..3 of the row, which depend on u
+  // only for 32-slot rows (through u % 2): NSRC distinct per-lane sources.
+  constexpr int NSRC = (C::NC == 32 && C::BPW > 1) ? 2 : 1;
+  const char* ksrc[NSRC];
+  const char* vsrc[NSRC];
+#pragma unroll
+  for (int u = 0; u < NSRC; ++u) {
+    const int n = 64 * (4 * u + wave) + lane;
+    const int r = n / C::NC;
+    const int c = (n % C::NC) ^ swz<D>(r);
+    ksrc[u] = kbase + 16 * c;
+    vsrc[u] = vbase + 16 * c;
+  }
+  auto issue_copy = [&](char* dk, char* dv, const int64_t* tab) __attribute__((always_inline)) {
+#pragma unroll
+    for (int u = 0; u < C::BPW; ++u) {
+      const int b = 4 * u + wave;
+      const int64_t off = tab[(64 * b + lane) / C::NC];
+      load_lds16(ksrc[u % NSRC] + off, dk + 1024 * b);
+      load_lds16(vsrc[u % NSRC] + off, dv + 1024 * b);
+    }
+  };
+
+  // fp8 caches: thread slot i = tid + 256 u is row i / NC, logical slot i % NC.
+  Stage<FP8, D> st;
+  auto stage_load = [&](const int64_t* tab) __attribute__((always_inline)) {
+    if constexpr (FP8) {
+#pragma unroll
+      for (int u = 0; u < C::CPT; ++u) {
+        const int i = tid + 256 * u;
+        const int64_t off = tab[i / C::NC] + 8 * (i % C::NC);
+        const u32x2 a = *reinterpret_cast<const u32x2*>(kbase + off);
+        const u32x2 b = *reinterpret_cast<const u32x2*>(vbase + off);
+        st.k[u][0] = a[0]; st.k[u][1] = a[1];
+        st.v[u][0] = b[0]; st.v[u][1] = b[1];
+      }
+    }
+  };
+  auto stage_store = [&](char* dk, char* dv) __attribute__((always_inline)) {
+    if constexpr (FP8) {
+#pragma unroll
+      for (int u = 0; u < C::CPT; ++u) {
+        const int i = tid + 256 * u;
+        const int r = i / C::NC;
+        const int at = r * ROWB + 16 * ((i % C::NC) ^ swz<D>(r));
+        *reinterpret_cast<u32x4*>(dk + at) = fp8x8_to<QT>(u32x2{st.k[u][0], st.k[u][1]});
+        *reinterpret_cast<u32x4*>(dv + at) = fp8x8_to<QT>(u32x2{st.v[u][0], st.v[u][1]});
+      }
+    }
+  };
+
+  // LDS read addresses (bytes within a tile buffer).
+  // K operand of MFMA c of key block kb: row 32 kb + l32, logical slot 2c + g2.
+  int kaddr[C::QC];
+  {
+    const int f = swz<D>(l32);
+#pragma unroll
+    for (int c = 0; c < C::QC; ++c) kaddr[c] = l32 * ROWB + 16 * ((2 * c + g2) ^ f);
+  }
+  // V^T operand of output block d, keys 16 kk + {0..7} (hh = 0) / {8..15}
+  // (hh = 1): lane reads row 16 kk + 4 g2 + s16 / 4 + 8 hh, bytes
+  // 64 d + 32 (q16 & 1) + 8 (s16 & 3) of the logical row.
+  const int s16 = lane & 15, q16 = lane >> 4;
+  int vaddr[2][C::DB];
+#pragma unroll
+  for (int hh = 0; hh < 2; ++hh) {
+    const int r = 4 * g2 + (s16 >> 2) + 8 * hh;
+    const int f = swz<D>(r);
+#pragma unroll
+    for (int d = 0; d < C::DB; ++d) {
+      const int lc = 4 * d + 2 * (q16 & 1) + ((s16 & 3) >> 1);
+      vaddr[hh][d] = r * ROWB + 16 * (lc ^ f) + 8 * (s16 & 1);
+    }
+  }
+
   const int ntiles = (k1 - k0 + TK - 1) / TK;
-  Stage<QT, FP8, D> st;
-  stage_load<QT, FP8, D>(st, p, bt_row, sm_pg, pg_first, kbase, vbase, k0, kl, k1, tid);
-  stage_store<QT, FP8, D>(st, sK[0], sV[0], tid);
-  __syncthreads();
 
-  for (int t = 0; t < ntiles; ++t) {
-    const int kt = k0 + t * TK;
-    const int buf = t & 1;
-    if (t + 1 < ntiles)
-      stage_load<QT, FP8, D>(st, p, bt_row, sm_pg, pg_first, kbase, vbase, kt + TK, kl, k1, tid);
-
-    if (wave_live) {
-      const uint16_t* sk = sK[buf];
-      const uint16_t* sv = sV[buf];
-      // ---- S^T = K Q^T
-      f32x16 sacc[C::KB];
+  auto compute = [&](const char* sk, const char* sv, int kt) __attribute__((always_inline)) {
+    // ---- S^T = K Q^T
+    f32x16 sacc[C::KB];
 #pragma unroll
-      for (int kb = 0; kb < C::KB; ++kb) {
-        sacc[kb] = f32x16{};
-        const int key = 32 * kb + l32;
+    for (int kb = 0; kb < C::KB; ++kb) {
+      sacc[kb] = f32x16{};
 #pragma unroll
-        for (int c = 0; c < C::QC; ++c) {
-          const u32x4 a = *reinterpret_cast<const u32x4*>(sk + lds_off<D>(key, 2 * c + g2));
-          sacc[kb] = mfma32<QT>(a, qop[c], sacc[kb]);
-        }
+      for (int c = 0; c < C::QC; ++c) {
+        const u32x4 a = *reinterpret_cast<const u32x4*>(sk + 32 * kb * ROWB + kaddr[c]);
+        sacc[kb] = mfma32<QT>(a, qop[c], sacc[kb]);
       }
-      // ---- logits and masks.  Without softcap/ALiBi the raw dot products are
-      // kept (cs = scale * log2 e is applied in the FMA feeding exp2); with them
-      // the base-2 logits are formed here (cs = 1).
-      const bool full = kt >= kl && kt + TK <= k1 && kt + TK - 1 <= wave_pmin &&
-                        (p.window <= 0 || kt > wave_pmax - p.window);
-      float cs = c2;
-      if (general) {
-        cs = 1.0f;
+    }
+    // ---- logits and masks.  Without softcap/ALiBi the raw dot products are
+    // kept (cs = scale * log2 e is applied in the FMA feeding exp2); with them
+    // the base-2 logits are formed here (cs = 1).
+    const bool full = kt >= kl && kt + TK <= k1 && kt + TK - 1 <= wave_pmin &&
+                      (p.window <= 0 || kt > wave_pmax - p.window);
+    float cs = c2;
+    // key of register r of block kb: kt + 32 kb + 8 (r / 4) + 4 g2 + r % 4;
+    // visible iff row_lo <= key < row_hi, tested as one unsigned compare.
+    const uint32_t span = (uint32_t)max(row_hi - row_lo, 0);
+    const int kd0 = kt + 4 * g2 - row_lo;
+    if (general) {
+      // Base-2 logits (softcap or plain scale), then the ALiBi bias and the
+      // mask in one shared pass.
+      cs = 1.0f;
+      if (p.softcap_on) {
 #pragma unroll
         for (int kb = 0; kb < C::KB; ++kb)
 #pragma unroll
           for (int r = 0; r < 16; ++r) {
-            const int key = kt + 32 * kb + 8 * (r >> 2) + 4 * g2 + (r & 3);
-            const float raw = sacc[kb][r];
-            float v = p.softcap_on ? p.cap_out2 * tanh_fast(raw * p.cap_in) : raw * c2;
-            v += slope2 * (float)(key - ctx);
-            sacc[kb][r] = (key >= row_lo && key < row_hi) ? v : -INFINITY;
+            sacc[kb][r] = p.cap_out2 * tanh_fast(sacc[kb][r] * p.cap_in);
+            // Keep the scheduler from interleaving all 16 tanh chains.
+            if ((r & 3) == 3) __builtin_amdgcn_sched_barrier(0);
           }
-      } else if (!full) {
+      } else {
 #pragma unroll
         for (int kb = 0; kb < C::KB; ++kb)
 #pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const int key = kt + 32 * kb + 8 * (r >> 2) + 4 * g2 + (r & 3);
-            sacc[kb][r] = (key >= row_lo && key < row_hi) ? sacc[kb][r] : -INFINITY;
-          }
+          for (int r = 0; r < 16; ++r) sacc[kb][r] *= c2;
       }
-      float mt = -INFINITY;
+      const float al0 = slope2 * (float)(kt + 4 * g2 - ctx);
 #pragma unroll
       for (int kb = 0; kb < C::KB; ++kb)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) mt = fmaxf(mt, sacc[kb][r]);
-      // Row maximum across the lane pair (l, l ^ 32) holding the same row,
-      // in base-2 logit units (cs > 0, and -inf stays -inf).
-      mt = wave_max_xor(mt, 32) * cs;
-      // Move the running maximum only when this tile exceeds it by > 8 (base 2).
-      const bool need = mt > m_run + 8.0f;
-      if (__builtin_amdgcn_ballot_w64(need)) {
-        const float m_new = need ? mt : m_run;
-        const float alpha = need ? fast_exp2(m_run - m_new) : 1.0f;  // m_run = -inf -> 0
-        l_run *= alpha;
-#pragma unroll
-        for (int d = 0; d < C::DB; ++d) oacc[d] *= alpha;
-        m_run = m_new;
-      }
-      const float m_use = (m_run == -INFINITY) ? 0.0f : m_run;
-      // ---- P = 2^(s * cs - m), packed as the B operands of the PV MFMAs
-      u32x4 pop[TK / 16];
-      float psum = 0.0f;
-#pragma unroll
-      for (int kk = 0; kk < TK / 16; ++kk) {
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const float a = fast_exp2(__builtin_fmaf(sacc[kk >> 1][8 * (kk & 1) + 2 * q], cs, -m_use));
-          const float b =
-              fast_exp2(__builtin_fmaf(sacc[kk >> 1][8 * (kk & 1) + 2 * q + 1], cs, -m_use));
-          psum += a + b;
-          pop[kk][q] = pack2<QT>(a, b);
+        for (int r = 0; r < 16; ++r) {
+          const int o = 32 * kb + 8 * (r >> 2) + (r & 3);
+          const float v = sacc[kb][r] + __builtin_fmaf(slope2, (float)o, al0);
+          sacc[kb][r] = (uint32_t)(kd0 + o) < span ? v : -INFINITY;
         }
-      }
-      l_run += psum;
-      // ---- O^T += V^T P^T
-      const int s16 = lane & 15, q16 = lane >> 4;
+    } else if (!full) {
 #pragma unroll
-      for (int d = 0; d < C::DB; ++d) {
-        const int dcol = 32 * d + 16 * (q16 & 1) + 4 * (s16 & 3);
+      for (int kb = 0; kb < C::KB; ++kb)
 #pragma unroll
-        for (int kk = 0; kk < TK / 16; ++kk) {
-          const int key0 = 16 * kk + 4 * g2 + (s16 >> 2);
-          const u32x2 lo2 = lds_read_tr16(sv + key0 * C::PITCH + dcol);
-          const u32x2 hi2 = lds_read_tr16(sv + (key0 + 8) * C::PITCH + dcol);
-          oacc[d] = mfma32<QT>(u32x4{lo2[0], lo2[1], hi2[0], hi2[1]}, pop[kk], oacc[d]);
+        for (int r = 0; r < 16; ++r) {
+          const int o = 32 * kb + 8 * (r >> 2) + (r & 3);
+          sacc[kb][r] = (uint32_t)(kd0 + o) < span ? sacc[kb][r] : -INFINITY;
         }
+    }
+    float mt = -INFINITY;
+#pragma unroll
+    for (int kb = 0; kb < C::KB; ++kb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) mt = fmaxf(mt, sacc[kb][r]);
+    // Row maximum across the lane pair (l, l ^ 32) holding the same row,
+    // in base-2 logit units (cs > 0, and -inf stays -inf).
+    mt = wave_max_xor(mt, 32) * cs;
+    // Move the running maximum only when this tile exceeds it by > 8 (base 2).
+    const bool need = mt > m_run + 8.0f;
+    if (__builtin_amdgcn_ballot_w64(need)) {
+      const float m_new = need ? mt : m_run;
+      const float alpha = need ? fast_exp2(m_run - m_new) : 1.0f;  // m_run = -inf -> 0
+      l_run *= alpha;
+#pragma unroll
+      for (int d = 0; d < C::DB; ++d) oacc[d] *= alpha;
+      m_run = m_new;
+    }
+    const float m_use = (m_run == -INFINITY) ? 0.0f : m_run;
+    // ---- P = 2^(s * cs - m), packed as the B operands of the PV MFMAs
+    u32x4 pop[TK / 16];
+    float psum = 0.0f;
+#pragma unroll
+    for (int kk = 0; kk < TK / 16; ++kk) {
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const float a = fast_exp2(__builtin_fmaf(sacc[kk >> 1][8 * (kk & 1) + 2 * q], cs, -m_use));
+        const float b =
+            fast_exp2(__builtin_fmaf(sacc[kk >> 1][8 * (kk & 1) + 2 * q + 1], cs, -m_use));
+        psum += a + b;
+        pop[kk][q] = pack2<QT>(a, b);
       }
     }
-    if (t + 1 < ntiles) stage_store<QT, FP8, D>(st, sK[buf ^ 1], sV[buf ^ 1], tid);
+    l_run += psum;
+    // ---- O^T += V^T P^T
+#pragma unroll
+    for (int d = 0; d < C::DB; ++d) {
+#pragma unroll
+      for (int kk = 0; kk < TK / 16; ++kk) {
+        const u32x2 lo2 = lds_read_tr16(sv + 16 * kk * ROWB + vaddr[0][d]);
+        const u32x2 hi2 = lds_read_tr16(sv + 16 * kk * ROWB + vaddr[1][d]);
+        oacc[d] = mfma32<QT>(u32x4{lo2[0], lo2[1], hi2[0], hi2[1]}, pop[kk], oacc[d]);
+      }
+    }
+  };
+
+  // Prologue: tables of tiles 0 and 1, then tile 0 into buffer 0.
+  if (wave == 0) fill_tab(sTab0, k0);
+  if (wave == 1 && ntiles > 1) fill_tab(sTab1, k0 + TK);
+  __syncthreads();
+  if constexpr (FP8) {
+    stage_load(sTab0);
+    stage_store(sK0, sV0);
+  } else {
+    issue_copy(sK0, sV0, sTab0);
+    wait_vmem();
+  }
+  __syncthreads();
+
+  // Tile t lives in buffer t % 2 and its row table in table t % 2.  While it
+  // is computed, tile t + 1 is copied into the other buffer and one wave
+  // fills the table of tile t + 2 (the table tile t was copied with).
+  auto step = [&](auto bufc, int t) __attribute__((always_inline)) {
+    constexpr int B = decltype(bufc)::value;
+    char* cur_k = B ? sK1 : sK0;
+    char* cur_v = B ? sV1 : sV0;
+    char* nxt_k = B ? sK0 : sK1;
+    char* nxt_v = B ? sV0 : sV1;
+    const int64_t* tab_next = B ? sTab0 : sTab1;
+    int64_t* tab_fill = B ? sTab1 : sTab0;
+    const int kt = k0 + t * TK;
+    const bool more = t + 1 < ntiles;
+    if (more) {
+      if constexpr (FP8)
+        stage_load(tab_next);
+      else
+        issue_copy(nxt_k, nxt_v, tab_next);
+    }
+    if (t + 2 < ntiles && wave == (t & 3)) fill_tab(tab_fill, kt + 2 * TK);
+    if (wave_live) compute(cur_k, cur_v, kt);
+    if (more) {
+      if constexpr (FP8)
+        stage_store(nxt_k, nxt_v);
+      else
+        wait_vmem();
+    }
     __syncthreads();
+  };
+  for (int t = 0; t < ntiles; t += 2) {
+    step(std::integral_constant<int, 0>{}, t);
+    if (t + 1 < ntiles) step(std::integral_constant<int, 1>{}, t + 1);
   }
 
   if (!row_ok) return;
