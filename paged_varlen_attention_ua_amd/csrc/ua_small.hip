@@ -13,8 +13,8 @@
 //
 // Data flow per 32-key tile and wave (no LDS in the loop):
 //   * K rows go straight from HBM into registers already in the MFMA A-operand
-//     layout (lane l: key l % 16), and S^T = K Q^T comes out with one query row
-//     per lane (row = l % 16).
+//     layout (lane l: key key_of_row(l % 16)), and S^T = K Q^T comes out with
+//     one query row per lane (row = l % 16).
 //   * Because P^T then sits in the B-operand layout of O^T = V^T P^T, P stays
 //     in registers; the eight keys a lane contributes are the ones its S^T
 //     accumulator holds.
@@ -24,7 +24,9 @@
 //   * When block_size is a multiple of 16 each 16-key half tile lies in one
 //     cache block; the block-table entries of all of a wave's tiles are fetched
 //     in one lane-parallel load up front, so a tile's K/V loads never wait on a
-//     block-table load of their own.
+//     block-table load of their own.  Interior tiles then need no per-lane
+//     address arithmetic (a uniform half base plus fixed lane offsets) and run
+//     two deep: the next tile's loads are in flight while a tile is computed.
 //   * Logits are kept in the base-2 domain (pre-multiplied by log2 e, exp2 for
 //     the exponentials), the README's convention (section "2D vs 2D").
 
@@ -73,6 +75,13 @@ template <bool FP8, int D>
 __device__ __forceinline__ int kq_index(int c, int g) {
   return FP8 ? (D / 4) * g + 8 * c : 32 * c + 8 * g;
 }
+
+// Key order inside a 16-key half.  S^T row i of the QK MFMA (A-operand row
+// i, loaded by lanes with l % 16 == i) is key key_of_row(i) = 4 (i % 4) + i / 4,
+// so the four keys a lane group g holds in its S^T accumulator (rows 4g..4g+3)
+// are g, 4 + g, 8 + g, 12 + g, and the V rows a load instruction jj fetches for
+// lane groups 0..3 (keys 4 jj + g) are four adjacent cache slots.
+__device__ __forceinline__ int key_of_row(int i) { return 4 * (i & 3) + (i >> 2); }
 
 template <int QT, bool FP8, int D>
 struct Tile {
@@ -124,11 +133,36 @@ __device__ __forceinline__ void load_tile_paged16(Tile<QT, FP8, D>& t, const Par
   };
 #pragma unroll
   for (int hb = 0; hb < 2; ++hb) {
-    load_k_row<QT, FP8, D>(kbase + key_off(kt + 16 * hb + r16), g, t.k[hb]);
+    load_k_row<QT, FP8, D>(kbase + key_off(kt + 16 * hb + key_of_row(r16)), g, t.k[hb]);
 #pragma unroll
     for (int jj = 0; jj < 4; ++jj)
-      load_dw<C::VW>(vbase + key_off(kt + 16 * hb + 4 * g + jj) + C::E * r16 * C::EB,
+      load_dw<C::VW>(vbase + key_off(kt + 16 * hb + 4 * jj + g) + C::E * r16 * C::EB,
                      t.v[4 * hb + jj]);
+  }
+}
+
+// Tile loader for an interior tile (block_size % 16 == 0 and all 32 keys
+// loadable): half hb is slots slot0 .. slot0 + 15 of cache block page[hb], so
+// every address is a wave-uniform half base plus a fixed per-lane offset
+// (k_lane: key r16 and this lane's K pieces; v_lane[jj]: key 4g + jj and this
+// lane's 16-byte V piece).
+template <int QT, bool FP8, int D>
+__device__ __forceinline__ void load_tile_fast(Tile<QT, FP8, D>& t, const Params& p,
+                                               const char* kbase, const char* vbase, int kt,
+                                               const int32_t* page, uint32_t k_lane,
+                                               const uint32_t* v_lane) {
+  using C = SmallCfg<QT, FP8, D>;
+  const int64_t slot_b = p.kv_stride_slot * C::EB;
+  const int64_t blk_b = p.kv_stride_block * C::EB;
+#pragma unroll
+  for (int hb = 0; hb < 2; ++hb) {
+    const int kb0 = kt + 16 * hb;
+    const uint32_t bi = fastdiv((uint32_t)kb0, p.bs_div);
+    const int slot0 = kb0 - (int)bi * p.block_size;
+    const int64_t half = (int64_t)page[hb] * blk_b + (int64_t)slot0 * slot_b;
+    load_k_row<QT, FP8, D>(kbase + half + k_lane, 0, t.k[hb]);
+#pragma unroll
+    for (int jj = 0; jj < 4; ++jj) load_dw<C::VW>(vbase + half + v_lane[jj], t.v[4 * hb + jj]);
   }
 }
 
@@ -145,7 +179,7 @@ __device__ __forceinline__ void load_tile_any(Tile<QT, FP8, D>& t, const Params&
   for (int hb = 0; hb < 2; ++hb) {
     const int kb0 = kt + 16 * hb;
     {
-      const int key = kb0 + r16;
+      const int key = kb0 + key_of_row(r16);
       if (key >= kl && key < k1) {
         const uint32_t bi = fastdiv((uint32_t)key, p.bs_div);
         const int slot = key - (int)bi * p.block_size;
@@ -158,7 +192,7 @@ __device__ __forceinline__ void load_tile_any(Tile<QT, FP8, D>& t, const Params&
     }
 #pragma unroll
     for (int jj = 0; jj < 4; ++jj) {
-      const int key = kb0 + 4 * g + jj;
+      const int key = kb0 + 4 * jj + g;
       if (key >= kl && key < k1) {
         const uint32_t bi = fastdiv((uint32_t)key, p.bs_div);
         const int slot = key - (int)bi * p.block_size;
@@ -185,8 +219,8 @@ __device__ __forceinline__ u32x4 k_operand(const Tile<QT, FP8, D>& t, int hb, in
 }
 
 // A operand of the c-th PV MFMA (O^T = V^T P^T).  Lane l supplies
-// V[key_j][E*(l%16) + c] for its eight keys j (j < 4: 4g + j, else
-// 16 + 4g + j - 4), two keys per dword.
+// V[key_j][E*(l%16) + c] for its eight keys j (j < 4: 4j + g, else
+// 16 + 4(j - 4) + g: the keys its S^T accumulator holds), two keys per dword.
 template <int QT, bool FP8, int D>
 __device__ __forceinline__ u32x4 v_operand(const Tile<QT, FP8, D>& t, int c) {
   u32x4 op;
@@ -206,7 +240,7 @@ __device__ __forceinline__ u32x4 v_operand(const Tile<QT, FP8, D>& t, int c) {
 }
 
 template <int QT, bool FP8, int D, bool SPLIT, bool PAGE16>
-__global__ __launch_bounds__(64 * kSmallWaves, (D > 128 ? 2 : 3)) void small_kernel(Params p) {
+__global__ __launch_bounds__(64 * kSmallWaves, 2) void small_kernel(Params p) {
   using C = SmallCfg<QT, FP8, D>;
   constexpr int E = C::E;
   constexpr int QC = C::QC;
@@ -308,21 +342,38 @@ __global__ __launch_bounds__(64 * kSmallWaves, (D > 128 ? 2 : 3)) void small_ker
   const char* kbase = reinterpret_cast<const char*>(p.k) + kvh * p.kv_stride_head * C::EB;
   const char* vbase = reinterpret_cast<const char*>(p.v) + kvh * p.kv_stride_head * C::EB;
 
-  auto load = [&](Tile<QT, FP8, D>& t, int i) {
+  // Per-lane byte offsets inside a 16-key half (interior tiles).
+  const uint32_t slot_b32 = (uint32_t)(p.kv_stride_slot * C::EB);
+  const uint32_t k_lane = key_of_row(r16) * slot_b32 + kq_index<FP8, D>(0, g) * C::EB;
+  uint32_t v_lane[4];
+#pragma unroll
+  for (int jj = 0; jj < 4; ++jj) v_lane[jj] = (4 * jj + g) * slot_b32 + C::E * r16 * C::EB;
+
+  auto tile_pages = [&](int i, int32_t* page) __attribute__((always_inline)) {
+    if (i < kPreTiles) {
+      page[0] = __builtin_amdgcn_readfirstlane(sm_pg[wave][2 * i]);
+      page[1] = __builtin_amdgcn_readfirstlane(sm_pg[wave][2 * i + 1]);
+    } else {
+      page[0] = entry(2 * i);
+      page[1] = entry(2 * i + 1);
+    }
+  };
+  // Any tile (clamped loads; the first and last tile of a partition).
+  auto load = [&](Tile<QT, FP8, D>& t, int i) __attribute__((always_inline)) {
     const int kt = wk0 + kStride * i;
     if constexpr (PAGE16) {
       int32_t page[2];
-      if (i < kPreTiles) {
-        page[0] = __builtin_amdgcn_readfirstlane(sm_pg[wave][2 * i]);
-        page[1] = __builtin_amdgcn_readfirstlane(sm_pg[wave][2 * i + 1]);
-      } else {
-        page[0] = entry(2 * i);
-        page[1] = entry(2 * i + 1);
-      }
+      tile_pages(i, page);
       load_tile_paged16<QT, FP8, D>(t, p, kbase, vbase, kt, page, kl, k1, g, r16);
     } else {
       load_tile_any<QT, FP8, D>(t, p, bt_row, kbase, vbase, kt, kl, k1, g, r16);
     }
+  };
+  // Interior tile (PAGE16 only): all 32 keys loadable.
+  auto load_fast = [&](Tile<QT, FP8, D>& t, int i) __attribute__((always_inline)) {
+    int32_t page[2];
+    tile_pages(i, page);
+    load_tile_fast<QT, FP8, D>(t, p, kbase, vbase, wk0 + kStride * i, page, k_lane, v_lane);
   };
 
   f32x4 oacc[E];
@@ -345,7 +396,7 @@ __global__ __launch_bounds__(64 * kSmallWaves, (D > 128 ? 2 : 3)) void small_ker
     for (int hb = 0; hb < 2; ++hb) {
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        const int key = kt + 16 * hb + 4 * g + r;
+        const int key = kt + 16 * hb + 4 * r + g;
         const float raw = sacc[hb][r];
         float v = p.softcap_on ? p.cap_out2 * tanh_fast(raw * p.cap_in) : raw * p.qk_scale2;
         v += slope2 * (float)(key - ctx);
@@ -378,10 +429,51 @@ __global__ __launch_bounds__(64 * kSmallWaves, (D > 128 ? 2 : 3)) void small_ker
   // One tile per wave in flight; latency is hidden by running three waves per
   // SIMD (measured faster on MI355X than a two-tile register pipeline, whose
   // register pressure made the allocator reuse registers with loads in flight).
-  for (int i = 0; i < nt; ++i) {
-    Tile<QT, FP8, D> t1;
-    load(t1, i);
-    compute(t1, i);
+  if constexpr (PAGE16 && D <= 128) {
+    // Only a wave's first tile (partition or window start) and last tile
+    // (partition end) can be partial; the interior tiles run two deep: the
+    // next tile's loads are issued before the current tile is computed, and
+    // every load of a tile is issued before the first wait on any of them.
+    int i = 0;
+    if (nt > 0 && wk0 < kl) {
+      Tile<QT, FP8, D> t1;
+      load(t1, 0);
+      __builtin_amdgcn_sched_barrier(0);
+      compute(t1, 0);
+      i = 1;
+    }
+    const int ie = (nt > i && wk0 + kStride * (nt - 1) + kSmallTile > k1) ? nt - 1 : nt;
+    if (i < ie) {
+      Tile<QT, FP8, D> ta, tb;
+      load_fast(ta, i);
+      for (; i < ie; i += 2) {
+        if (i + 1 < ie) load_fast(tb, i + 1);
+        __builtin_amdgcn_sched_barrier(0);
+        compute(ta, i);
+        if (i + 1 >= ie) {
+          i += 1;
+          break;
+        }
+        if (i + 2 < ie) load_fast(ta, i + 2);
+        __builtin_amdgcn_sched_barrier(0);
+        compute(tb, i + 1);
+      }
+      i = ie;
+    }
+    if (i < nt) {
+      Tile<QT, FP8, D> t1;
+      load(t1, i);
+      __builtin_amdgcn_sched_barrier(0);
+      compute(t1, i);
+    }
+  } else {
+    // One tile in flight (D = 256: a second tile does not fit beside the
+    // accumulators; any block size: per-key block-table lookups).
+    for (int i = 0; i < nt; ++i) {
+      Tile<QT, FP8, D> t1;
+      load(t1, i);
+      compute(t1, i);
+    }
   }
 
   // Row state of this wave: m_run is already the row maximum across the four
