@@ -103,6 +103,17 @@ class Runner:
         self.pp = ctypes.byref(self.prob)
         self.pa = ctypes.byref(self.args)
 
+    def step_main(self, stream_ptr):
+        """The main kernel of a step only (one-pass or partition kernel)."""
+        B, lib = self.B, self.lib
+        if self.plan.path == B.UA_PATH_2D:
+            st = lib.ua_forward_2d(self.pp, ctypes.byref(self.plan), self.pa, stream_ptr)
+        else:
+            st = lib.ua_forward_splitkv(self.pp, ctypes.byref(self.plan), self.pa, self.ws_ptr,
+                                        self.ws_n, stream_ptr)
+        if st:
+            raise RuntimeError(f"launch status {st}")
+
     def step(self, stream_ptr, ev=None):
         """One pass: plan (host) + partition kernel (+ reduce).  ev = (start, end) events
         recorded around the main kernel only."""
@@ -135,10 +146,12 @@ def time_case(case, steps, warmup, path="auto", n_part=0, touched=None, kernel_e
               graph=True):
     """Time one workload over R rotated input copies.
 
-    Eager pass: every step is launched from the host; HIP events on the launch
-    stream bracket the main kernel of each step (kernel_ms).  Graph pass: R
-    steps (one per input copy) are captured once into a HIP graph and replayed,
-    so the per-step time is the GPU's, not the Python launcher's (ms_per_step).
+    Eager pass: every step is launched from the host (eager_ms_per_step).
+    Graph pass: R steps (one per input copy) are captured once into a HIP graph
+    and replayed, so the per-step time is the GPU's, not the Python launcher's
+    (ms_per_step).  Kernel pass: R launches of the main kernel alone (one-pass
+    or partition kernel, no reduce) captured and replayed the same way, timed
+    with HIP events on the replay stream (kernel_ms).
     """
     import torch
     from tests.gpu_common import to_device
@@ -189,6 +202,20 @@ def time_case(case, steps, warmup, path="auto", n_part=0, touched=None, kernel_e
         t1.record()
         torch.cuda.synchronize()
         ms = t0.elapsed_time(t1) / (reps * R)
+        if kernel_events:
+            gk = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(gk):
+                cap = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+                for r in runners:
+                    r.step_main(cap)
+            gk.replay()
+            torch.cuda.synchronize()
+            t0.record()
+            for _ in range(reps):
+                gk.replay()
+            t1.record()
+            torch.cuda.synchronize()
+            kms = t0.elapsed_time(t1) / (reps * R)
     plan = runners[0].plan
     return dict(ms_per_step=ms, eager_ms_per_step=eager_ms, kernel_ms=kms, path=int(plan.path),
                 n_part=int(plan.n_part), rotation_sets=R, kernel=int(plan.kernel))
