@@ -12,36 +12,40 @@
 namespace ua {
 namespace {
 
-// One 64-thread workgroup per row group: TPR threads own 4 head-dim values of
-// a row each.  Partition states are fetched U at a time with every load of a
-// batch issued before any is used, and merged online (running maximum), so
-// up to U partitions cost one memory round trip.
+// 256-thread workgroups; TPR threads own 8 head-dim values of a row each, so
+// one workgroup covers 256 / TPR rows.  Partition states are fetched U at a
+// time with every load of a batch issued before any is used, and merged online
+// (running maximum), so up to U partitions cost one memory round trip.
 template <int OT, int D>
-__global__ __launch_bounds__(64) void reduce_kernel(Params p) {
-  constexpr int TPR = D / 4;          // threads per row, 4 values each
-  constexpr int RPB = 64 / TPR;       // rows per workgroup
-  constexpr int U = 16;               // partitions fetched per batch
+__global__ __launch_bounds__(256) void reduce_kernel(Params p) {
+  constexpr int VPT = 8;              // values per thread
+  constexpr int TPR = D / VPT;        // threads per row
+  constexpr int RPB = 256 / TPR;      // rows per workgroup
+  constexpr int U = 8;                // partitions fetched per batch
   const int R = p.total_q * p.num_q_heads;
   const int tid = threadIdx.x;
-  const int64_t row = (int64_t)blockIdx.x * RPB + tid / TPR;
-  const int d0 = (tid % TPR) * 4;
+  const int row = blockIdx.x * RPB + tid / TPR;
+  const int d0 = (tid % TPR) * VPT;
   if (row >= R) return;
-  const int h = (int)(row % p.num_q_heads);
+  const int tok = row / p.num_q_heads;
+  const int h = row - tok * p.num_q_heads;
   const int P = p.n_part;
 
   float M = -INFINITY, L = 0.0f;
-  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+  f32x4 acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = {0.f, 0.f, 0.f, 0.f};
   for (int q0 = 0; q0 < P; q0 += U) {
     float mv[U], lv[U];
-    f32x4 av[U];
+    f32x4 a0[U], a1[U];
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       const int q = q0 + u;
       const bool in = q < P;
-      mv[u] = in ? p.ws_m[(int64_t)q * R + row] : -INFINITY;
-      lv[u] = in ? p.ws_l[(int64_t)q * R + row] : 0.0f;
-      av[u] = in ? *reinterpret_cast<const f32x4*>(p.ws_acc + ((int64_t)q * R + row) * D + d0)
-                 : f32x4{0.f, 0.f, 0.f, 0.f};
+      const int64_t qr = (int64_t)q * R + row;
+      mv[u] = in ? p.ws_m[qr] : -INFINITY;
+      lv[u] = in ? p.ws_l[qr] : 0.0f;
+      const float* src = p.ws_acc + qr * D + d0;
+      a0[u] = in ? *reinterpret_cast<const f32x4*>(src) : f32x4{0.f, 0.f, 0.f, 0.f};
+      a1[u] = in ? *reinterpret_cast<const f32x4*>(src + 4) : f32x4{0.f, 0.f, 0.f, 0.f};
     }
     float mb = M;
 #pragma unroll
@@ -49,14 +53,18 @@ __global__ __launch_bounds__(64) void reduce_kernel(Params p) {
     if (mb == -INFINITY) continue;  // nothing live yet
     const float f = fast_exp2(M - mb);  // M = -inf -> 0 (L and acc are 0 then)
     L *= f;
-    acc *= f;
+    acc0 *= f;
+    acc1 *= f;
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       const bool live = lv[u] > 0.0f;  // l == 0: acc and m are unspecified, never used
       const float w = live ? fast_exp2(mv[u] - mb) : 0.0f;
       L += w * lv[u];
 #pragma unroll
-      for (int e = 0; e < 4; ++e) acc[e] += live ? w * av[u][e] : 0.0f;
+      for (int e = 0; e < 4; ++e) {
+        acc0[e] += live ? w * a0[u][e] : 0.0f;
+        acc1[e] += live ? w * a1[u][e] : 0.0f;
+      }
     }
     M = mb;
   }
@@ -68,12 +76,19 @@ __global__ __launch_bounds__(64) void reduce_kernel(Params p) {
   L *= f;
   if (sink2 != -INFINITY) L += fast_exp2(sink2 - Ms);
   const float inv = any_key ? p.v_scale * f / L : 0.0f;
-  const int64_t tok = row / p.num_q_heads;
   char* dst = reinterpret_cast<char*>(p.out) +
-              (tok * p.o_stride_tok + (int64_t)h * p.o_stride_head + d0) * 2;
-  *reinterpret_cast<u32x2*>(dst) =
-      u32x2{pack2<OT>(acc[0] * inv, acc[1] * inv), pack2<OT>(acc[2] * inv, acc[3] * inv)};
+              ((int64_t)tok * p.o_stride_tok + (int64_t)h * p.o_stride_head + d0) * 2;
+  *reinterpret_cast<u32x4*>(dst) =
+      u32x4{pack2<OT>(acc0[0] * inv, acc0[1] * inv), pack2<OT>(acc0[2] * inv, acc0[3] * inv),
+            pack2<OT>(acc1[0] * inv, acc1[1] * inv), pack2<OT>(acc1[2] * inv, acc1[3] * inv)};
   if (p.lse != nullptr && d0 == 0) p.lse[row] = (L > 0.0f) ? (Ms + fast_log2(L)) * kLn2 : -INFINITY;
+}
+
+template <int OT, int D>
+void launch_reduce_d(const Params& p, int64_t R, hipStream_t stream) {
+  constexpr int RPB = 256 / (D / 8);
+  hipLaunchKernelGGL((reduce_kernel<OT, D>), dim3((unsigned)((R + RPB - 1) / RPB)), dim3(256), 0,
+                     stream, p);
 }
 
 template <int OT>
@@ -81,19 +96,10 @@ hipError_t launch_reduce_t(const Params& p, int head_dim, hipStream_t stream) {
   const int64_t R = (int64_t)p.total_q * p.num_q_heads;
   if (R == 0) return hipSuccess;
   switch (head_dim) {
-    case 64:
-      hipLaunchKernelGGL((reduce_kernel<OT, 64>), dim3((unsigned)((R + 3) / 4)), dim3(64), 0,
-                         stream, p);
-      break;
-    case 128:
-      hipLaunchKernelGGL((reduce_kernel<OT, 128>), dim3((unsigned)((R + 1) / 2)), dim3(64), 0,
-                         stream, p);
-      break;
-    case 256:
-      hipLaunchKernelGGL((reduce_kernel<OT, 256>), dim3((unsigned)R), dim3(64), 0, stream, p);
-      break;
-    default:
-      return hipErrorInvalidValue;
+    case 64: launch_reduce_d<OT, 64>(p, R, stream); break;
+    case 128: launch_reduce_d<OT, 128>(p, R, stream); break;
+    case 256: launch_reduce_d<OT, 256>(p, R, stream); break;
+    default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
 }
