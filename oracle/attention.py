@@ -25,6 +25,14 @@ What it computes is the plain definition, assembled from the pages:
 * ALiBi: slope_h * (j - ctx) added to the logit before the row maximum (README,
   section "2D vs 2D"; the pages give it in base 2 with a log2(e) factor, which is
   the same bias in natural units).
+* QQ-bias: ``qq_bias[i, j - ctx]`` added to the logit of query i (its index
+  inside the sequence's query chunk) for keys j >= ctx, i.e. a bias between the
+  chunk's own tokens, applied with ALiBi before the row maximum (README, section
+  "2D vs 2D", where the kernel adds it in base 2 with a 1/ln 2 factor).  The
+  pages give only the indexing and a row stride ("stride=256", README section
+  "Scenarios"); read here as one fp32 matrix with that row stride, shared by
+  every head and sequence, read only where j >= ctx (keys of the prefix get no
+  bias).
 * Sinks: one logit per query head that joins the softmax normaliser but carries
   no value row (README, section "Prefill-2D trace cohort": the sink is the
   initial running maximum).
@@ -73,6 +81,21 @@ def visible_mask(pos, kv_len, window):
     return vis
 
 
+def qq_terms(qq_bias, qi, rel):
+    """[n, kv] QQ-bias terms: qq_bias[qi, rel] where rel = j - ctx >= 0, else 0.
+
+    qi: [n] query indices inside the chunk; rel: [kv] key positions minus ctx.
+    Entries past the matrix (rel beyond its row, reachable only by keys the
+    causal mask hides) contribute 0 as well.
+    """
+    qq = np.asarray(qq_bias, dtype=np.float64)
+    rel = np.asarray(rel)
+    ok = (rel >= 0) & (rel < qq.shape[1])
+    cols = np.where(ok, rel, 0)
+    t = qq[np.asarray(qi)[:, None], cols[None, :]]
+    return np.where(ok[None, :], t, 0.0)
+
+
 def row_attention(x, vis, V, sink):
     """Two-pass softmax attention of a block of rows over one head.
 
@@ -103,13 +126,14 @@ def row_attention(x, vis, V, sink):
 def attention(q, k_cache, v_cache, block_table, cu_seqlens_q, seq_lens, *,
               q_dtype, kv_dtype, block_size, scale, num_q_heads, num_kv_heads,
               window=0, softcap=0.0, alibi_slopes=None, sinks=None,
-              k_scale=1.0, v_scale=1.0, rows=None, **_unused):
+              k_scale=1.0, v_scale=1.0, rows=None, qq_bias=None, **_unused):
     """Plain-definition attention in float64.
 
     q: stored bits [total_q, Hq, D]; k_cache/v_cache: stored bits
     [num_blocks, block_size, Hkv, D]; block_table int [num_seqs, max_blocks];
     cu_seqlens_q int [num_seqs + 1]; seq_lens int [num_seqs].
     rows: optional sorted array of query-token indices to compute (default all).
+    qq_bias: optional float [rows >= max q_len, stride] matrix (natural units).
     Returns (out [n_rows, Hq, D], lse [n_rows, Hq]) in float64, rows in the
     order of ``rows``.  lse includes the sink term; -inf where nothing is seen.
     """
@@ -143,6 +167,8 @@ def attention(q, k_cache, v_cache, block_table, cu_seqlens_q, seq_lens, *,
                     x = softcap * np.tanh(x / softcap)
                 if alibi_slopes is not None:
                     x = x + float(alibi_slopes[h]) * rel[None, :]
+                if qq_bias is not None:
+                    x = x + qq_terms(qq_bias, tok - q0, rel)
                 sink = None if sinks is None else float(sinks[h])
                 o, l = row_attention(x, vis, V[:, g, :], sink)
                 out[idx, h, :] = o

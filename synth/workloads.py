@@ -9,7 +9,9 @@ Recipe (one ``numpy.random.Generator(PCG64(seed))`` per case, fixed draw order):
 1. kv lengths that are drawn from a range (uniform integers, inclusive);
 2. a permutation of the physical blocks;
 3. Q, then K, then V as float32 N(0, 1) ("values N(0,1)" in every workload);
-4. sink logits N(0, 1) when sinks are on.
+4. sink logits N(0, 1) when sinks are on;
+5. the QQ-bias matrix N(0, 1) when it is on: float32 [max(max q_len, 1), stride]
+   (one matrix for every head and sequence, row stride ``stride``).
 
 The cache holds ``2 * N`` blocks where N = sum ceil(kv_len / block_size) blocks
 are needed; the logical blocks of all sequences, in (sequence, block) order,
@@ -64,13 +66,14 @@ def alibi_slopes_pow2(num_heads):
 def make_case(*, seqs, head_dim, num_q_heads, num_kv_heads, block_size,
               q_dtype="f16", kv_dtype=None, o_dtype=None, seed=0,
               kv_range=None, num_seqs=None, q_len=None,
-              window=0, softcap=0.0, alibi=False, sinks=False,
+              window=0, softcap=0.0, alibi=False, sinks=False, qq_bias=False,
               poison=True, scale=None, extra_pad_cols=1, cache_factor=2):
     """Build one seeded case.
 
     ``seqs``: list of (q_len, kv_len) pairs, or None to draw ``num_seqs`` kv
     lengths uniformly from ``kv_range`` (inclusive) with the given ``q_len``.
     ``alibi``: False, True (2^(-8i/H) slopes) or an explicit slope array.
+    ``qq_bias``: False, True (row stride 256) or the row stride as an int.
     Returns a dict whose keys match the oracle's and the binding's arguments.
     """
     kv_dtype = kv_dtype or q_dtype
@@ -104,6 +107,13 @@ def make_case(*, seqs, head_dim, num_q_heads, num_kv_heads, block_size,
     kf = rng.standard_normal((N, block_size, Hk, D), dtype=np.float32)
     vf = rng.standard_normal((N, block_size, Hk, D), dtype=np.float32)
     sink_vals = rng.standard_normal(H, dtype=np.float32) if sinks else None
+    qq = None
+    if qq_bias is not False and qq_bias is not None:
+        stride = 256 if qq_bias is True else int(qq_bias)
+        rows = max(int(q_lens.max()) if n_seqs else 0, 1)
+        if stride < rows:
+            raise ValueError("qq_bias stride must cover the longest query chunk")
+        qq = rng.standard_normal((rows, stride), dtype=np.float32)
 
     k_scale = v_scale = 1.0
     if kv_dtype == "e4m3fn":
@@ -142,7 +152,7 @@ def make_case(*, seqs, head_dim, num_q_heads, num_kv_heads, block_size,
     return dict(
         q=_round_storage(qf, q_dtype), k_cache=k_cache, v_cache=v_cache,
         block_table=block_table, cu_seqlens_q=cu, seq_lens=kv_lens.astype(np.int32),
-        alibi_slopes=slopes, sinks=sink_vals,
+        alibi_slopes=slopes, sinks=sink_vals, qq_bias=qq,
         q_dtype=q_dtype, kv_dtype=kv_dtype, o_dtype=o_dtype,
         block_size=block_size, head_dim=D, num_q_heads=H, num_kv_heads=Hk,
         scale=float(scale if scale is not None else 1.0 / math.sqrt(D)),

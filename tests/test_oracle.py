@@ -2,10 +2,12 @@
 
 * format decoders: closed-form codes and library decoders (numpy float16, torch
   bfloat16 / float8_e4m3fn) over every code;
-* the hand-worked example in tests/golden/hand_example.json;
+* the hand-worked examples in tests/golden/hand_example.json and
+  tests/golden/qq_bias_example.json;
 * a brute-force loop implementation written independently below, on tiny
   random problems with every feature combination;
-* torch's float64 scaled_dot_product_attention for the dense special case;
+* torch's float64 scaled_dot_product_attention for the dense special case
+  (also with a QQ-bias passed as its additive float mask);
 * closed forms (all-zero keys, geometric ALiBi weights, two-key softcap) and
   invariants (window >= kv_len, window 1, block-table permutation, batching,
   partition merge for any partition count).
@@ -141,7 +143,8 @@ def _val(s):
     if isinstance(s, (int, float)):
         return float(s)
     return float(eval(s, {"ln2": math.log(2), "ln3": math.log(3), "ln4": math.log(4),
-                          "ln8": math.log(8), "log2": math.log2}))
+                          "ln5": math.log(5), "ln7": math.log(7), "ln8": math.log(8),
+                          "ln11": math.log(11), "log2": math.log2}))
 
 
 def _hand_case(case, inp):
@@ -189,6 +192,19 @@ def test_hand_example_merge():
     assert abs(lse[0] - _val(case["lse"])) < 1e-12
 
 
+def test_qq_bias_hand_example():
+    g = json.load(open(os.path.join(os.path.dirname(GOLDEN), "qq_bias_example.json")))
+    inp = g["inputs"]
+    K = np.array(inp["keys"], dtype=np.float32)[:, None, :]
+    V = np.array(inp["values"], dtype=np.float32)[:, None, :]
+    Q = np.zeros((inp["q_len"], 1, 2), dtype=np.float32)
+    qq = np.array([[_val(x) for x in row] for row in inp["qq_bias"]])
+    c = paged_problem([(K, V)], [Q], block_size=2, extra=dict(scale=1.0, qq_bias=qq))
+    o, lse = attention(**c)
+    np.testing.assert_allclose(o[:, 0, :], np.array(g["out"]), rtol=0, atol=1e-12)
+    np.testing.assert_allclose(lse[:, 0], [_val(x) for x in g["lse"]], rtol=0, atol=1e-12)
+
+
 # ----------------------------------------------------------------------------- brute force
 
 def _dec_lib(bits, dtype):
@@ -213,6 +229,7 @@ def brute_force(c):
     cap = c.get("softcap", 0.0)
     slopes = c.get("alibi_slopes")
     sinks = c.get("sinks")
+    qq = c.get("qq_bias")
     out = np.zeros(qf.shape)
     cu = c["cu_seqlens_q"]
     for s in range(len(c["seq_lens"])):
@@ -235,6 +252,8 @@ def brute_force(c):
                         x = cap * math.tanh(x / cap)
                     if slopes is not None:
                         x += float(slopes[h]) * (j - (kv - ql))
+                    if qq is not None and j >= kv - ql:
+                        x += float(qq[i][j - (kv - ql)])
                     logits.append(x)
                     vals.append(vf[blk, j % bs, g])
                 if not logits:
@@ -256,6 +275,8 @@ FEATURES = [
     dict(sinks=True),
     dict(window=5, softcap=2.0, sinks=True),
     dict(window=4, alibi=True),
+    dict(qq_bias=24),
+    dict(qq_bias=20, alibi=True, softcap=1.5, window=6),
 ]
 
 
@@ -299,6 +320,54 @@ def test_oracle_matches_torch_sdpa_fp64(G):
     mask = torch.ones(L, L, dtype=torch.bool).tril()  # q_len == kv_len: bottom-right == top-left
     ref = torch.nn.functional.scaled_dot_product_attention(qt, kt, vt, attn_mask=mask, scale=0.3)
     np.testing.assert_allclose(o, ref[0].permute(1, 0, 2).numpy(), rtol=0, atol=1e-12)
+
+
+@pytest.mark.parametrize("G", [1, 4])
+def test_qq_bias_matches_torch_sdpa_float_mask(G):
+    """q_len == kv_len (ctx = 0): the QQ-bias is SDPA's additive float mask on the
+    causal triangle (qq[i][j] for j <= i, -inf above)."""
+    rng = np.random.default_rng(6)
+    Hk, D, L, stride = 2, 8, 29, 40
+    K = rng.standard_normal((L, Hk, D)).astype(np.float16).astype(np.float32)
+    V = rng.standard_normal((L, Hk, D)).astype(np.float16).astype(np.float32)
+    Q = rng.standard_normal((L, G * Hk, D)).astype(np.float16).astype(np.float32)
+    qq = rng.standard_normal((L, stride))
+    c = paged_problem([(K, V)], [Q], block_size=3, extra=dict(scale=0.4, qq_bias=qq))
+    o, _ = attention(**c)
+    qt = torch.from_numpy(Q.astype(np.float64)).permute(1, 0, 2)[None]
+    kt = torch.from_numpy(K.astype(np.float64)).permute(1, 0, 2).repeat_interleave(G, 0)[None]
+    vt = torch.from_numpy(V.astype(np.float64)).permute(1, 0, 2).repeat_interleave(G, 0)[None]
+    fm = torch.full((L, L), float("-inf"), dtype=torch.float64)
+    tri = torch.ones(L, L, dtype=torch.bool).tril()
+    fm[tri] = torch.from_numpy(qq[:, :L])[tri]
+    ref = torch.nn.functional.scaled_dot_product_attention(qt, kt, vt, attn_mask=fm, scale=0.4)
+    np.testing.assert_allclose(o, ref[0].permute(1, 0, 2).numpy(), rtol=0, atol=1e-12)
+
+
+def test_qq_bias_linear_rows_equal_alibi_without_prefix():
+    """ctx = 0: qq[i][c] = slope * c for every row is ALiBi with that slope (one
+    head), and a row-constant bias cancels in the softmax."""
+    rng = np.random.default_rng(8)
+    L, D, slope = 23, 4, 0.37
+    K = rng.standard_normal((L, 1, D)).astype(np.float32)
+    V = rng.standard_normal((L, 1, D)).astype(np.float32)
+    Q = rng.standard_normal((L, 1, D)).astype(np.float32)
+    qq = np.tile(slope * np.arange(32, dtype=np.float64), (L, 1))
+    base = paged_problem([(K, V)], [Q], block_size=4, extra=dict(scale=0.5))
+    o_qq, _ = attention(**dict(base, qq_bias=qq))
+    o_al, _ = attention(**dict(base, alibi_slopes=np.array([slope])))
+    np.testing.assert_allclose(o_qq, o_al, rtol=0, atol=1e-12)
+    rowc = np.tile(rng.standard_normal((L, 1)), (1, 32))
+    o_rc, _ = attention(**dict(base, qq_bias=rowc))
+    o_0, _ = attention(**base)
+    np.testing.assert_allclose(o_rc, o_0, rtol=0, atol=1e-12)
+    # with a prefix the bias reaches only the chunk's keys: a row-constant bias
+    # then shifts weight from the prefix to the chunk
+    Qc = Q[-5:]
+    pre = paged_problem([(K, V)], [Qc], block_size=4, extra=dict(scale=0.5))
+    o_p0, _ = attention(**pre)
+    o_p1, _ = attention(**dict(pre, qq_bias=np.full((5, 8), 3.0)))
+    assert np.abs(o_p1 - o_p0).max() > 1e-3
 
 
 # ----------------------------------------------------------------------------- closed forms
