@@ -86,14 +86,16 @@ class Runner:
             num_seqs=len(case["seq_lens"]), max_seqlen_q=case["max_seqlen_q"],
             max_seqlen_k=case["max_seqlen_k"], scale=case["scale"], softcap=case["softcap"],
             window=case["window"], k_scale=case["k_scale"], v_scale=case["v_scale"],
-            alibi_slopes=dev["alibi_slopes"], sinks=dev["sinks"], out=self.out)
+            alibi_slopes=dev["alibi_slopes"], sinks=dev["sinks"], out=self.out,
+            qq_bias=dev.get("qq_bias"))
         self.force = {"auto": B.UA_PATH_AUTO, "2d": B.UA_PATH_2D, "splitkv": B.UA_PATH_SPLITKV}[path]
         self.n_part = n_part
         self.ncu = A.num_cus(dev["q"].device)
         self.plan = B.ua_plan(self.prob, self.ncu, self.force, n_part)
         self.args = A.make_args(dev["q"], dev["k_cache"], dev["v_cache"], dev["block_table"],
                                 dev["cu_seqlens_q"], dev["seq_lens"], self.out,
-                                alibi_slopes=dev["alibi_slopes"], sinks=dev["sinks"])
+                                alibi_slopes=dev["alibi_slopes"], sinks=dev["sinks"],
+                                qq_bias=dev.get("qq_bias"))
         nbytes = max(int(self.plan.workspace_bytes), 256)
         self.ws = torch.empty(nbytes, dtype=torch.uint8, device=dev["q"].device)
         self.ws_ptr = ctypes.c_void_p(self.ws.data_ptr())
@@ -419,9 +421,16 @@ def main():
                          "path": "splitkv" if rr["path"] == 2 else "2d",
                          "kernel": "large" if rr["kernel"] == 1 else "small"}
         line["prefill"] = pre
-        mixed = make_case(**WORKLOADS["mixed_fp16_d128_16q2kv"], poison=False)
-        rr = time_case(mixed, args.steps, args.warmup, kernel_events=False)
-        line["mixed_fp16_d128_16q2kv_us_per_step"] = round(rr["ms_per_step"] * 1e3, 2)
+        lat = {}
+        for name in ["mixed_fp16_d128_16q2kv", "mixed_fp16_d128_16q2kv_alibi",
+                     "qq_bias_prefill_fp16_d128_16q2kv"]:
+            c = make_case(**WORKLOADS[name], poison=False)
+            rr = time_case(c, args.steps, args.warmup, kernel_events=False)
+            lat[name] = {"us_per_step": round(rr["ms_per_step"] * 1e3, 2),
+                         "TFLOP/s": round(prefill_flops(c) / (rr["ms_per_step"] * 1e-3) / 1e12, 2),
+                         "path": "splitkv" if rr["path"] == 2 else "2d",
+                         "kernel": "large" if rr["kernel"] == 1 else "small"}
+        line["latency_bound"] = lat
     if not args.no_cpu:
         line["cpu_baseline"] = cpu_baseline(make_case(**WORKLOADS[HEADLINE]))
     print(json.dumps(line), flush=True)

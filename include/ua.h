@@ -53,7 +53,7 @@
 extern "C" {
 #endif
 
-#define UA_ABI_VERSION 1
+#define UA_ABI_VERSION 2
 
 typedef enum { UA_F16 = 0, UA_BF16 = 1, UA_FP8_E4M3FN = 2 } ua_dtype;
 
@@ -94,6 +94,15 @@ typedef struct {
   int64_t q_stride_tok, q_stride_head;
   int64_t o_stride_tok, o_stride_head;
   int64_t kv_stride_block, kv_stride_slot, kv_stride_head;
+  /* QQ-bias (RocKE unified_attention README, sections "Scenarios" and "2D vs
+   * 2D"): when has_qq_bias, args->qq_bias is one fp32 matrix shared by every
+   * head and sequence, row stride qq_bias_stride elements, at least
+   * max_seqlen_q rows; qq_bias[i * stride + (j - ctx)] (natural-log units) is
+   * added to the logit of query i of a sequence's chunk for keys j >= ctx
+   * (ctx = kv_len - q_len), after softcap and with ALiBi.  Requires
+   * qq_bias_stride >= max_seqlen_q. */
+  int32_t has_qq_bias;
+  int32_t qq_bias_stride;
 } ua_problem;
 
 /* Output of ua_plan; treat as opaque except path, n_part and workspace_bytes. */
@@ -122,6 +131,8 @@ typedef struct {
   float* lse;                  /* optional [total_q, Hq] fp32 log-sum-exp (natural log,
                                   sink included; -inf for a row that sees nothing
                                   and has no sink), or NULL */
+  const float* qq_bias;        /* [>= max_seqlen_q, qq_bias_stride] fp32 or NULL
+                                  (must match has_qq_bias) */
 } ua_args;
 
 /*

@@ -30,8 +30,10 @@ def num_cus(device):
 
 def make_problem(q, k_cache, v_cache, block_table, *, num_seqs, max_seqlen_q, max_seqlen_k,
                  scale, softcap=0.0, window=0, k_scale=1.0, v_scale=1.0, alibi_slopes=None,
-                 sinks=None, out=None):
-    """ua_problem for Q [total_q, Hq, D], caches [num_blocks, block_size, Hkv, D]."""
+                 sinks=None, out=None, qq_bias=None):
+    """ua_problem for Q [total_q, Hq, D], caches [num_blocks, block_size, Hkv, D].
+
+    qq_bias: optional [rows, stride] fp32 matrix (row-contiguous)."""
     total_q, Hq, D = q.shape
     nb, bs, Hkv, Dk = k_cache.shape
     if Dk != D or tuple(v_cache.shape) != tuple(k_cache.shape):
@@ -62,6 +64,13 @@ def make_problem(q, k_cache, v_cache, block_table, *, num_seqs, max_seqlen_q, ma
     p.v_scale = v_scale
     p.has_alibi = 1 if alibi_slopes is not None else 0
     p.has_sinks = 1 if sinks is not None else 0
+    if qq_bias is not None:
+        if qq_bias.dim() != 2 or qq_bias.stride(1) != 1:
+            raise ValueError("qq_bias must be a 2-D matrix with contiguous rows")
+        if qq_bias.shape[0] < max(max_seqlen_q, 1):
+            raise ValueError("qq_bias needs at least max_seqlen_q rows")
+        p.has_qq_bias = 1
+        p.qq_bias_stride = qq_bias.stride(0)
     p.q_stride_tok, p.q_stride_head = q.stride(0), q.stride(1)
     p.o_stride_tok, p.o_stride_head = o.stride(0), o.stride(1)
     p.kv_stride_block, p.kv_stride_slot, p.kv_stride_head = k_cache.stride()[:3]
@@ -69,7 +78,7 @@ def make_problem(q, k_cache, v_cache, block_table, *, num_seqs, max_seqlen_q, ma
 
 
 def make_args(q, k_cache, v_cache, block_table, cu_seqlens_q, seq_lens, out, lse=None,
-              alibi_slopes=None, sinks=None):
+              alibi_slopes=None, sinks=None, qq_bias=None):
     for name, t, dt in (("block_table", block_table, torch.int32),
                         ("cu_seqlens_q", cu_seqlens_q, torch.int32),
                         ("seq_lens", seq_lens, torch.int32)):
@@ -78,6 +87,8 @@ def make_args(q, k_cache, v_cache, block_table, cu_seqlens_q, seq_lens, out, lse
     for name, t in (("alibi_slopes", alibi_slopes), ("sinks", sinks), ("lse", lse)):
         if t is not None and (t.dtype != torch.float32 or not t.is_contiguous()):
             raise ValueError(f"{name} must be contiguous float32")
+    if qq_bias is not None and qq_bias.dtype != torch.float32:
+        raise ValueError("qq_bias must be float32")
     a = B.UaArgs()
     a.q, a.k_cache, a.v_cache = q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr()
     a.block_table, a.cu_seqlens_q = block_table.data_ptr(), cu_seqlens_q.data_ptr()
@@ -86,6 +97,7 @@ def make_args(q, k_cache, v_cache, block_table, cu_seqlens_q, seq_lens, out, lse
     a.sinks = sinks.data_ptr() if sinks is not None else None
     a.out = out.data_ptr()
     a.lse = lse.data_ptr() if lse is not None else None
+    a.qq_bias = qq_bias.data_ptr() if qq_bias is not None else None
     return a
 
 
@@ -104,7 +116,7 @@ def workspace(nbytes, device, stream):
 def forward(q, k_cache, v_cache, block_table, cu_seqlens_q, seq_lens, *, max_seqlen_q,
             max_seqlen_k, scale, softcap=0.0, window=0, k_scale=1.0, v_scale=1.0,
             alibi_slopes=None, sinks=None, out=None, lse=None, path="auto", n_part=0,
-            ws=None):
+            ws=None, qq_bias=None):
     """Unified paged varlen attention; returns (out, plan).
 
     path: "auto" (dispatcher), "2d" (one pass) or "splitkv" (partitions + reduce).
@@ -118,10 +130,10 @@ def forward(q, k_cache, v_cache, block_table, cu_seqlens_q, seq_lens, *, max_seq
     prob = make_problem(q, k_cache, v_cache, block_table, num_seqs=num_seqs,
                         max_seqlen_q=max_seqlen_q, max_seqlen_k=max_seqlen_k, scale=scale,
                         softcap=softcap, window=window, k_scale=k_scale, v_scale=v_scale,
-                        alibi_slopes=alibi_slopes, sinks=sinks, out=out)
+                        alibi_slopes=alibi_slopes, sinks=sinks, out=out, qq_bias=qq_bias)
     plan = B.ua_plan(prob, num_cus(q.device), _PATH[path], n_part)
     args = make_args(q, k_cache, v_cache, block_table, cu_seqlens_q, seq_lens, out, lse,
-                     alibi_slopes, sinks)
+                     alibi_slopes, sinks, qq_bias)
     stream = torch.cuda.current_stream(q.device)
     sp = ctypes.c_void_p(stream.cuda_stream)
     if plan.path == B.UA_PATH_2D:

@@ -39,6 +39,7 @@ class UaProblem(ctypes.Structure):
         ("o_stride_tok", ctypes.c_int64), ("o_stride_head", ctypes.c_int64),
         ("kv_stride_block", ctypes.c_int64), ("kv_stride_slot", ctypes.c_int64),
         ("kv_stride_head", ctypes.c_int64),
+        ("has_qq_bias", ctypes.c_int32), ("qq_bias_stride", ctypes.c_int32),
     ]
 
 
@@ -57,6 +58,7 @@ class UaArgs(ctypes.Structure):
         ("block_table", ctypes.c_void_p), ("cu_seqlens_q", ctypes.c_void_p),
         ("seq_lens", ctypes.c_void_p), ("alibi_slopes", ctypes.c_void_p),
         ("sinks", ctypes.c_void_p), ("out", ctypes.c_void_p), ("lse", ctypes.c_void_p),
+        ("qq_bias", ctypes.c_void_p),
     ]
 
 

@@ -10,6 +10,7 @@
 // host integers only (max_seqlen_q / max_seqlen_k), never a device sync.
 
 #include <cmath>
+#include <algorithm>
 #include <cstring>
 
 #include "ua_internal.h"
@@ -39,7 +40,8 @@ uint64_t problem_hash(const ua_problem* p) {
   hs.add(p->softcap); hs.add(p->window); hs.add(p->k_scale); hs.add(p->v_scale);
   hs.add(p->has_alibi); hs.add(p->has_sinks); hs.add(p->q_stride_tok); hs.add(p->q_stride_head);
   hs.add(p->o_stride_tok); hs.add(p->o_stride_head); hs.add(p->kv_stride_block);
-  hs.add(p->kv_stride_slot); hs.add(p->kv_stride_head);
+  hs.add(p->kv_stride_slot); hs.add(p->kv_stride_head); hs.add(p->has_qq_bias);
+  hs.add(p->qq_bias_stride);
   return hs.h;
 }
 
@@ -80,6 +82,7 @@ ua_status validate(const ua_problem* p) {
     return UA_EUNSUPPORTED;
   if (p->kv_stride_block % kv_vec || p->kv_stride_slot % kv_vec || p->kv_stride_head % kv_vec)
     return UA_EUNSUPPORTED;
+  if (p->has_qq_bias && p->qq_bias_stride < std::max(p->max_seqlen_q, 1)) return UA_EINVAL;
   const int G = p->num_q_heads / p->num_kv_heads;
   if (G > kLargeRows) return UA_EUNSUPPORTED;
   if (!(p->scale > 0.f)) return UA_EUNSUPPORTED;
@@ -94,6 +97,7 @@ ua_status check_args(const ua_problem* p, const ua_args* a) {
     return UA_EINVAL;
   if ((p->has_alibi != 0) != (a->alibi_slopes != nullptr)) return UA_EINVAL;
   if ((p->has_sinks != 0) != (a->sinks != nullptr)) return UA_EINVAL;
+  if ((p->has_qq_bias != 0) != (a->qq_bias != nullptr)) return UA_EINVAL;
   auto aligned = [](const void* ptr, uintptr_t n) { return ((uintptr_t)ptr % n) == 0; };
   if (!aligned(a->q, 16) || !aligned(a->out, 16) || !aligned(a->k_cache, 16) ||
       !aligned(a->v_cache, 16))
@@ -122,6 +126,8 @@ Params make_params(const ua_problem* p, const ua_plan_t* plan, const ua_args* a,
   q.sinks = a->sinks;
   q.out = a->out;
   q.lse = a->lse;
+  q.qq_bias = p->has_qq_bias ? a->qq_bias : nullptr;
+  q.qq_stride = p->has_qq_bias ? p->qq_bias_stride : 0;
   if (ws) {
     const int64_t R = (int64_t)p->total_q * p->num_q_heads;
     char* base = reinterpret_cast<char*>(ws);

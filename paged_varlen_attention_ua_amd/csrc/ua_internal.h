@@ -51,6 +51,7 @@ struct Params {
   const float* sinks;  // [Hq] or null
   void* out;
   float* lse;  // [total_q, Hq] or null
+  const float* qq_bias;  // [>= max q_len, qq_stride] or null
   float* ws_m;
   float* ws_l;
   float* ws_acc;
@@ -71,6 +72,7 @@ struct Params {
   int32_t softcap_on;
   int32_t grid_x;       // number of query-block slots launched along x
   int32_t seq_blocks;   // 1: block x is the sequence index (every query run fits one block)
+  int32_t qq_stride;    // QQ-bias row stride (elements)
 };
 
 // Launchers (defined next to their kernels).  Return hipError_t of the launch.

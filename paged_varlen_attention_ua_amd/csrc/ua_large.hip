@@ -191,7 +191,7 @@ __global__ __launch_bounds__(256, (D > 128 ? 1 : 2)) void large_kernel(Params p)
   const int row_lo = p.window > 0 ? max(kl, pos - p.window + 1) : kl;
   const int row_hi = min(k1, pos + 1);
   const float slope2 = (p.alibi != nullptr && row_ok) ? p.alibi[h] * kLog2e : 0.0f;
-  const bool general = p.softcap_on || p.alibi != nullptr;
+  const bool general = p.softcap_on || p.alibi != nullptr || p.qq_bias != nullptr;
 
   // Q as the B operand of S^T = K Q^T: lane holds Q[row][16c + 8*g2 .. + 8].
   u32x4 qop[C::QC];
@@ -370,6 +370,20 @@ __global__ __launch_bounds__(256, (D > 128 ? 1 : 2)) void large_kernel(Params p)
           const float v = sacc[kb][r] + __builtin_fmaf(slope2, (float)o, al0);
           sacc[kb][r] = (uint32_t)(kd0 + o) < span ? v : -INFINITY;
         }
+      // QQ-bias qq[i][key - ctx] (i = this row's index in its chunk) on the
+      // chunk's own keys; tiles wholly inside the prefix skip it.
+      if (p.qq_bias != nullptr && kt + TK > ctx && row_ok) {
+        const float* qrow = p.qq_bias + (int64_t)(pos - ctx) * p.qq_stride;
+        const int rel0 = kt + 4 * g2 - ctx;
+#pragma unroll
+        for (int kb = 0; kb < C::KB; ++kb)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int rel = rel0 + 32 * kb + 8 * (r >> 2) + (r & 3);
+            const float b = (uint32_t)rel < (uint32_t)p.qq_stride ? qrow[rel] : 0.0f;
+            sacc[kb][r] = __builtin_fmaf(b, kLog2e, sacc[kb][r]);
+          }
+      }
     } else if (!full) {
 #pragma unroll
       for (int kb = 0; kb < C::KB; ++kb)

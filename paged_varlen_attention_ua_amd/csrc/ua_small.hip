@@ -391,7 +391,6 @@ __global__ __launch_bounds__(64 * kSmallWaves, 2) void small_kernel(Params p) {
       for (int c = 0; c < QC; ++c) sacc[hb] = mfma16<QT>(k_operand(t, hb, c), qop[c], sacc[hb]);
     }
     float x[8];
-    float mt = -INFINITY;
 #pragma unroll
     for (int hb = 0; hb < 2; ++hb) {
 #pragma unroll
@@ -399,9 +398,30 @@ __global__ __launch_bounds__(64 * kSmallWaves, 2) void small_kernel(Params p) {
         const int key = kt + 16 * hb + 4 * r + g;
         const float raw = sacc[hb][r];
         float v = p.softcap_on ? p.cap_out2 * tanh_fast(raw * p.cap_in) : raw * p.qk_scale2;
-        v += slope2 * (float)(key - ctx);
+        x[4 * hb + r] = v + slope2 * (float)(key - ctx);
+      }
+    }
+    // QQ-bias qq[i][key - ctx] (i = this row's index in its chunk) on the
+    // chunk's own keys; tiles wholly inside the prefix skip it.
+    if (p.qq_bias != nullptr && kt + kSmallTile > ctx) {
+      const float* qrow = p.qq_bias + (int64_t)(row_ok ? pos - ctx : 0) * p.qq_stride;
+#pragma unroll
+      for (int hb = 0; hb < 2; ++hb)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int rel = kt + 16 * hb + 4 * r + g - ctx;
+          const float b = (row_ok && (uint32_t)rel < (uint32_t)p.qq_stride) ? qrow[rel] : 0.0f;
+          x[4 * hb + r] = __builtin_fmaf(b, kLog2e, x[4 * hb + r]);
+        }
+    }
+    float mt = -INFINITY;
+#pragma unroll
+    for (int hb = 0; hb < 2; ++hb) {
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int key = kt + 16 * hb + 4 * r + g;
         const bool vis = key >= row_lo && key < row_hi;
-        x[4 * hb + r] = vis ? v : -INFINITY;
+        x[4 * hb + r] = vis ? x[4 * hb + r] : -INFINITY;
         mt = fmaxf(mt, x[4 * hb + r]);
       }
     }

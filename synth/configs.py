@@ -36,6 +36,11 @@ C5C = dict(C5A, seqs=[(1024, 1024)] * 4, seed=125)
 C5D = dict(seqs=[(8192, 8192)], head_dim=256, num_q_heads=24, num_kv_heads=4,
            block_size=784, q_dtype="bf16", seed=135)
 
+# QQ-bias scenario of the RocKE README ("qq_bias_prefill_d128_b16": the
+# prefill_d128_b16 sequences with a QQ-bias of row stride 256).
+QQ = dict(seqs=[(64, 64), (128, 256), (32, 256)], head_dim=128, num_q_heads=16,
+          num_kv_heads=2, block_size=16, q_dtype="f16", qq_bias=256, seed=106)
+
 WORKLOADS = {
     "decode_fp16_d128_16q2kv": C1,
     "mixed_fp16_d128_16q2kv": C2,
@@ -48,6 +53,7 @@ WORKLOADS = {
     "prefill_chunk2k_prefix16k_bf16": C5B,
     "prefill_4x1k_bf16": C5C,
     "prefill_8k_d256_24q4kv_bs784_bf16": C5D,
+    "qq_bias_prefill_fp16_d128_16q2kv": QQ,
 }
 
 DECODE_WORKLOADS = [

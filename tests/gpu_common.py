@@ -49,6 +49,8 @@ def to_device(case, device="cuda"):
                       else torch.from_numpy(np.asarray(case["alibi_slopes"], np.float32)).to(device)),
         sinks=(None if case["sinks"] is None
                else torch.from_numpy(np.asarray(case["sinks"], np.float32)).to(device)),
+        qq_bias=(None if case.get("qq_bias") is None
+                 else torch.from_numpy(np.asarray(case["qq_bias"], np.float32)).to(device)),
     )
     return d
 
@@ -72,7 +74,7 @@ def run(case, dev=None, path="auto", n_part=0, lse=False, poison_out=True, ws=No
                         scale=case["scale"], softcap=case["softcap"], window=case["window"],
                         k_scale=case["k_scale"], v_scale=case["v_scale"],
                         alibi_slopes=dev["alibi_slopes"], sinks=dev["sinks"], out=out,
-                        lse=lse_t, path=path, n_part=n_part, ws=ws)
+                        lse=lse_t, path=path, n_part=n_part, ws=ws, qq_bias=dev.get("qq_bias"))
     torch.cuda.synchronize()
     res = o.float().cpu().numpy().astype(np.float64)
     l = lse_t.cpu().numpy().astype(np.float64) if lse_t is not None else None

@@ -33,14 +33,15 @@ def test_library_exports_every_declared_symbol():
     lib = ctypes.CDLL(B.LIB_PATH)
     for fn in _declared_functions():
         assert hasattr(lib, fn), fn
-    assert U.ua_abi_version() == 1
+    assert U.ua_abi_version() == 2
 
 
 def test_struct_sizes_match_header_layout():
-    # ua_problem: 6 int32, int64, 3 int32, 3 int32, 2 float, int32, 2 float, 2 int32, pad, 7 int64
-    assert ctypes.sizeof(B.UaProblem) == 144
+    # ua_problem: 6 int32, int64, 3 int32, 3 int32, 2 float, int32, 2 float, 2 int32, pad,
+    # 7 int64, 2 int32 (QQ-bias)
+    assert ctypes.sizeof(B.UaProblem) == 152
     assert ctypes.sizeof(B.UaPlan) == 48
-    assert ctypes.sizeof(B.UaArgs) == 80
+    assert ctypes.sizeof(B.UaArgs) == 88
 
 
 def problem(**kw):
@@ -121,6 +122,8 @@ def test_grid_covers_every_query_block():
     (dict(kv_stride_slot=1028), -2),
     (dict(q_stride_head=0), -1),
     (dict(total_q=9), -1),
+    (dict(has_qq_bias=1, qq_bias_stride=0), -1),
+    (dict(max_seqlen_q=300, total_q=8, has_qq_bias=1, qq_bias_stride=256), -1),
 ])
 def test_invalid_problems_are_rejected(kw, code):
     st, _ = status_of(problem(**kw))

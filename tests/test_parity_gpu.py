@@ -137,6 +137,33 @@ def test_features_visible_at_tolerance(path, n_part):
         _check(case, path, n_part, label=str(kw))
 
 
+@pytest.mark.parametrize("path,n_part", [("auto", 0), ("2d", 0), ("splitkv", 3)])
+def test_qq_bias_scenario(path, n_part):
+    """The README's QQ-bias prefill scenario (row stride 256) through both kernels."""
+    case, ref, ref_lse = _workload("qq_bias_prefill_fp16_d128_16q2kv")
+    print(f"[case] qq_bias path={path} n_part={n_part}", flush=True)
+    got, lse, plan = run(case, _dev("qq_bias_prefill_fp16_d128_16q2kv"), path=path,
+                         n_part=n_part, lse=True)
+    compare(case, got, ref, label=f"qq/{path}{n_part}")
+    check_lse(lse, ref_lse, label="qq")
+
+
+@pytest.mark.parametrize("path,n_part", [("2d", 0), ("splitkv", 3)])
+def test_qq_bias_with_other_features(path, n_part):
+    """QQ-bias on decode rows (small kernel), mixed chunks and prefixes (large
+    kernel), combined with ALiBi, softcap, sinks and a window, bf16 and fp8 KV."""
+    seqs = [(1, 40), (3, 6), (70, 300), (5, 60), (0, 9), (129, 129)]
+    for kw in [dict(), dict(alibi=True, softcap=2.5), dict(sinks=True, window=50),
+               dict(kv_dtype="e4m3fn", o_dtype="bf16", q_dtype="bf16")]:
+        base = dict(BASE)
+        base.update({k: v for k, v in kw.items() if k in ("q_dtype",)})
+        rest = {k: v for k, v in kw.items() if k not in ("q_dtype",)}
+        case = make_case(seqs=seqs, seed=51, qq_bias=160, **base, **rest)
+        _check(case, path, n_part, label=f"qq+{kw}")
+    dec = make_case(seqs=[(1, 700), (1, 33), (2, 90)], seed=52, qq_bias=8, **BASE)
+    _check(dec, path, n_part, label="qq-decode")
+
+
 def test_split_partition_counts_agree():
     """Split-KV with any partition count equals one pass (within tolerance, pairwise)."""
     case, ref, _ = _workload("long_decode_bf16_d128_32q8kv_w4096_softcap_sinks")
