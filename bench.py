@@ -397,7 +397,9 @@ def main():
         others = {}
         for name in ["decode_fp16_d128_16q2kv", "fp8kv_decode_b32_ctx590",
                      "fp8kv_decode_b8_ctx6700_w4096",
-                     "long_decode_bf16_d128_32q8kv_w4096_softcap_sinks"]:
+                     "long_decode_bf16_d128_32q8kv_w4096_softcap_sinks",
+                     "decode_64k_bf16_d128_32q8kv", "decode_mqa_bf16_d128_32q1kv",
+                     "decode_d256_fp16_16q2kv", "decode_fp16_d128_16q2kv_bs64"]:
             c = make_case(**WORKLOADS[name], poison=False)
             rr = time_case(c, args.steps, args.warmup, kernel_events=False)
             b = decode_bytes(c)
@@ -409,7 +411,9 @@ def main():
         line["decode_other"] = others
         pre = {}
         for name in ["prefill_chunk1k_prefix8k_bf16", "prefill_chunk2k_prefix16k_bf16",
-                     "prefill_4x1k_bf16", "prefill_8k_d256_24q4kv_bs784_bf16"]:
+                     "prefill_4x1k_bf16", "prefill_8k_d256_24q4kv_bs784_bf16",
+                     "d64_chunked_prefill_bf16_64q8kv_bs32_sinks_w128",
+                     "d64_prefill_bf16q_fp8kv_64q8kv_bs32_sinks"]:
             c = make_case(**WORKLOADS[name], poison=False)
             fl = prefill_flops(c)
             rr = time_case(c, max(5, args.steps // 5), 3, touched=decode_bytes(c),

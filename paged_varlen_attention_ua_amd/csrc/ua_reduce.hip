@@ -12,33 +12,38 @@
 namespace ua {
 namespace {
 
-// 256-thread workgroups; TPR threads own 8 head-dim values of a row each, so
-// one workgroup covers 256 / TPR rows.  Partition states are fetched U at a
-// time with every load of a batch issued before any is used, and merged online
-// (running maximum), so up to U partitions cost one memory round trip.
-template <int OT, int D>
+// 256-thread workgroups.  A row is owned by SP groups of TPR threads; a thread
+// owns 8 head-dim values, and group g merges partitions g, g + SP, g + 2 SP, ...
+// (SP > 1 when a row has many partitions, so that few rows still spread over
+// many threads).  Within a group, partition states are fetched U at a time
+// with every load of a batch issued before any is used, and merged online
+// (running maximum); the SP group states of a row are then merged through LDS.
+template <int OT, int D, int SP>
 __global__ __launch_bounds__(256) void reduce_kernel(Params p) {
   constexpr int VPT = 8;              // values per thread
-  constexpr int TPR = D / VPT;        // threads per row
-  constexpr int RPB = 256 / TPR;      // rows per workgroup
+  constexpr int TPR = D / VPT;        // threads per row and group
+  constexpr int RPB = 256 / (TPR * SP);  // rows per workgroup
   constexpr int U = 8;                // partitions fetched per batch
+  __shared__ float sm_m[SP > 1 ? RPB * SP : 1];
+  __shared__ float sm_l[SP > 1 ? RPB * SP : 1];
+  __shared__ __attribute__((aligned(16))) float sm_acc[SP > 1 ? RPB * SP * D : 1];
   const int R = p.total_q * p.num_q_heads;
   const int tid = threadIdx.x;
-  const int row = blockIdx.x * RPB + tid / TPR;
+  const int rl = tid / (TPR * SP);
+  const int grp = (tid / TPR) % SP;
+  const int row = blockIdx.x * RPB + rl;
   const int d0 = (tid % TPR) * VPT;
-  if (row >= R) return;
-  const int tok = row / p.num_q_heads;
-  const int h = row - tok * p.num_q_heads;
+  const bool valid = row < R;
   const int P = p.n_part;
 
   float M = -INFINITY, L = 0.0f;
   f32x4 acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = {0.f, 0.f, 0.f, 0.f};
-  for (int q0 = 0; q0 < P; q0 += U) {
+  for (int q0 = grp; valid && q0 < P; q0 += U * SP) {
     float mv[U], lv[U];
     f32x4 a0[U], a1[U];
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-      const int q = q0 + u;
+      const int q = q0 + u * SP;
       const bool in = q < P;
       const int64_t qr = (int64_t)q * R + row;
       mv[u] = in ? p.ws_m[qr] : -INFINITY;
@@ -68,6 +73,45 @@ __global__ __launch_bounds__(256) void reduce_kernel(Params p) {
     }
     M = mb;
   }
+  if constexpr (SP > 1) {
+    // Group states of each row -> LDS; group 0 folds the other groups in.
+    const int slot = rl * SP + grp;
+    if ((tid % TPR) == 0) {
+      sm_m[slot] = M;
+      sm_l[slot] = L;
+    }
+    *reinterpret_cast<f32x4*>(sm_acc + slot * D + d0) = acc0;
+    *reinterpret_cast<f32x4*>(sm_acc + slot * D + d0 + 4) = acc1;
+    __syncthreads();
+    if (grp != 0) return;
+    float Mg = -INFINITY;
+#pragma unroll
+    for (int g = 0; g < SP; ++g)
+      Mg = sm_l[rl * SP + g] > 0.0f ? fmaxf(Mg, sm_m[rl * SP + g]) : Mg;
+    L = 0.0f;
+    acc0 = f32x4{0.f, 0.f, 0.f, 0.f};
+    acc1 = f32x4{0.f, 0.f, 0.f, 0.f};
+    if (Mg != -INFINITY) {
+#pragma unroll
+      for (int g = 0; g < SP; ++g) {
+        const int sl = rl * SP + g;
+        const float lg = sm_l[sl];
+        const float w = lg > 0.0f ? fast_exp2(sm_m[sl] - Mg) : 0.0f;
+        L += w * lg;
+        const f32x4 b0 = *reinterpret_cast<const f32x4*>(sm_acc + sl * D + d0);
+        const f32x4 b1 = *reinterpret_cast<const f32x4*>(sm_acc + sl * D + d0 + 4);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          acc0[e] += lg > 0.0f ? w * b0[e] : 0.0f;
+          acc1[e] += lg > 0.0f ? w * b1[e] : 0.0f;
+        }
+      }
+    }
+    M = Mg;
+  }
+  if (!valid) return;
+  const int tok = row / p.num_q_heads;
+  const int h = row - tok * p.num_q_heads;
   const bool any_key = L > 0.0f;
   const float sink2 = (p.sinks != nullptr) ? p.sinks[h] * kLog2e : -INFINITY;
   const float Mt = fmaxf(M, sink2);
@@ -84,11 +128,24 @@ __global__ __launch_bounds__(256) void reduce_kernel(Params p) {
   if (p.lse != nullptr && d0 == 0) p.lse[row] = (L > 0.0f) ? (Ms + fast_log2(L)) * kLn2 : -INFINITY;
 }
 
+template <int OT, int D, int SP>
+void launch_reduce_sp(const Params& p, int64_t R, hipStream_t stream) {
+  constexpr int RPB = 256 / ((D / 8) * SP);
+  hipLaunchKernelGGL((reduce_kernel<OT, D, SP>), dim3((unsigned)((R + RPB - 1) / RPB)), dim3(256),
+                     0, stream, p);
+}
+
+// Groups per row: one batch of 8 partitions per group where possible.
 template <int OT, int D>
 void launch_reduce_d(const Params& p, int64_t R, hipStream_t stream) {
-  constexpr int RPB = 256 / (D / 8);
-  hipLaunchKernelGGL((reduce_kernel<OT, D>), dim3((unsigned)((R + RPB - 1) / RPB)), dim3(256), 0,
-                     stream, p);
+  if (p.n_part <= 8)
+    launch_reduce_sp<OT, D, 1>(p, R, stream);
+  else if (p.n_part <= 16)
+    launch_reduce_sp<OT, D, 2>(p, R, stream);
+  else if (p.n_part <= 32)
+    launch_reduce_sp<OT, D, 4>(p, R, stream);
+  else
+    launch_reduce_sp<OT, D, 8>(p, R, stream);
 }
 
 template <int OT>

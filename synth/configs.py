@@ -41,6 +41,28 @@ C5D = dict(seqs=[(8192, 8192)], head_dim=256, num_q_heads=24, num_kv_heads=4,
 QQ = dict(seqs=[(64, 64), (128, 256), (32, 256)], head_dim=128, num_q_heads=16,
           num_kv_heads=2, block_size=16, q_dtype="f16", qq_bias=256, seed=106)
 
+# Second workload family (RocKE README, "Prefill-2D trace cohort"): head size
+# 64, block size 32, 64 query / 8 kv heads, attention sinks, sliding window
+# (127, 0) -- 127 keys to the left plus the query's own, W = 128 here -- or full,
+# bf16 or bf16 Q with fp8 KV, chunked prefill over many sequences.  The serving
+# traces themselves are not available; these are synthetic shapes of that kind.
+D64_SW = dict(seqs=[(256, 2048)] * 16, head_dim=64, num_q_heads=64, num_kv_heads=8,
+              block_size=32, q_dtype="bf16", window=128, sinks=True, seed=201)
+D64_FP8 = dict(seqs=[(1024, 5120)] * 4, head_dim=64, num_q_heads=64, num_kv_heads=8,
+               block_size=32, q_dtype="bf16", kv_dtype="e4m3fn", o_dtype="bf16",
+               sinks=True, seed=202)
+
+# Decode variants the README's scenario sets name (section "Scenarios":
+# decode_d256_b16, decode_d128_b64, and the long-context / MQA decode of the
+# "creative" set).
+DEC_64K = dict(seqs=[(1, 65536)] * 4, head_dim=128, num_q_heads=32, num_kv_heads=8,
+               block_size=16, q_dtype="bf16", seed=203)
+DEC_MQA = dict(seqs=None, num_seqs=8, q_len=1, kv_range=(6500, 6900), head_dim=128,
+               num_q_heads=32, num_kv_heads=1, block_size=16, q_dtype="bf16", seed=204)
+DEC_D256 = dict(seqs=[(1, 1024), (1, 2048)], head_dim=256, num_q_heads=16, num_kv_heads=2,
+                block_size=16, q_dtype="f16", seed=205)
+DEC_B64 = dict(C1, block_size=64, seed=206)
+
 WORKLOADS = {
     "decode_fp16_d128_16q2kv": C1,
     "mixed_fp16_d128_16q2kv": C2,
@@ -54,7 +76,24 @@ WORKLOADS = {
     "prefill_4x1k_bf16": C5C,
     "prefill_8k_d256_24q4kv_bs784_bf16": C5D,
     "qq_bias_prefill_fp16_d128_16q2kv": QQ,
+    "d64_chunked_prefill_bf16_64q8kv_bs32_sinks_w128": D64_SW,
+    "d64_prefill_bf16q_fp8kv_64q8kv_bs32_sinks": D64_FP8,
+    "decode_64k_bf16_d128_32q8kv": DEC_64K,
+    "decode_mqa_bf16_d128_32q1kv": DEC_MQA,
+    "decode_d256_fp16_16q2kv": DEC_D256,
+    "decode_fp16_d128_16q2kv_bs64": DEC_B64,
 }
+
+NEXT_DECODE_WORKLOADS = [
+    "decode_64k_bf16_d128_32q8kv",
+    "decode_mqa_bf16_d128_32q1kv",
+    "decode_d256_fp16_16q2kv",
+    "decode_fp16_d128_16q2kv_bs64",
+]
+NEXT_PREFILL_WORKLOADS = [
+    "d64_chunked_prefill_bf16_64q8kv_bs32_sinks_w128",
+    "d64_prefill_bf16q_fp8kv_64q8kv_bs32_sinks",
+]
 
 DECODE_WORKLOADS = [
     "decode_fp16_d128_16q2kv",

@@ -74,6 +74,41 @@ def test_prefill_full_size_sampled_rows(name, path, n_part):
     print(f"[ok] {name} path={plan.path} max_abs={err:.3e}", flush=True)
 
 
+NEXT_DECODE = ["decode_64k_bf16_d128_32q8kv", "decode_mqa_bf16_d128_32q1kv",
+               "decode_d256_fp16_16q2kv", "decode_fp16_d128_16q2kv_bs64"]
+NEXT_PREFILL = ["d64_chunked_prefill_bf16_64q8kv_bs32_sinks_w128",
+                "d64_prefill_bf16q_fp8kv_64q8kv_bs32_sinks"]
+
+
+@pytest.mark.parametrize("path,n_part", [("auto", 0), ("2d", 0), ("splitkv", 4)])
+@pytest.mark.parametrize("name", NEXT_DECODE)
+def test_next_decode_workloads(name, path, n_part):
+    """64K-context, MQA (G = 32, large-block kernel), d256 and block-size-64 decode."""
+    case, ref, ref_lse = _workload(name)
+    print(f"[case] {name} path={path} n_part={n_part}", flush=True)
+    got, lse, plan = run(case, _dev(name), path=path, n_part=n_part, lse=True)
+    err = compare(case, got, ref, label=f"{name}/{path}{n_part}")
+    check_lse(lse, ref_lse, label=name)
+    print(f"[ok] {name} kernel={plan.kernel} path={plan.path} n_part={plan.n_part} "
+          f"max_abs={err:.3e}", flush=True)
+
+
+@pytest.mark.parametrize("path,n_part", [("auto", 0), ("splitkv", 2)])
+@pytest.mark.parametrize("name", NEXT_PREFILL)
+def test_next_prefill_workloads_sampled_rows(name, path, n_part):
+    """d64 / block 32 / GQA-8 chunked prefill with sinks and window 128, and the
+    bf16-Q + fp8-KV variant."""
+    case = make_case(**WORKLOADS[name])
+    rows = sample_rows(case["q"].shape[0], 64, seed=9)
+    ref, ref_lse = oracle.attention(**case, rows=rows)
+    print(f"[case] {name} path={path} rows={len(rows)}", flush=True)
+    got, lse, plan = run(case, path=path, n_part=n_part, lse=True)
+    assert np.isfinite(got).all(), "unwritten or NaN output rows"
+    err = compare(case, got, ref, rows=rows, label=name)
+    check_lse(lse[rows], ref_lse, label=name)
+    print(f"[ok] {name} path={plan.path} max_abs={err:.3e}", flush=True)
+
+
 # ----------------------------------------------------------------------------- edge cases
 
 def _check(case, path="auto", n_part=0, lse=True, label=""):
