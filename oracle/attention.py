@@ -40,8 +40,10 @@ What it computes is the plain definition, assembled from the pages:
   knob, README section "Scenarios", but never define it; this is the plainest
   reading and is applied before ALiBi).
 * Grouped-query heads: q head h reads kv head h // (Hq / Hkv).
-* fp8 KV: stored E4M3 codes times a per-tensor fp32 scale (AITER PR #3962,
-  section "Testing").
+* fp8 KV: stored E4M3 codes (OCP e4m3fn or e4m3fnuz) times a per-tensor fp32
+  scale, and, when given, times a per-token fp32 scale of the key's (block,
+  slot, kv head) (AITER PR #3962, section "Testing": both dialects, per-tensor
+  and per-token scales).  Both factors apply when both are given.
 * Empty rows: a query that sees no key returns zeros (AITER PR #3962, review
   reply: rows with seq_len 0 return zeros).
 
@@ -57,18 +59,27 @@ from .formats import decode
 _ROW_CHUNK = 256  # rows per matmul; only bounds memory, every row is independent
 
 
-def gather_kv(cache_bits, kv_dtype, block_table_row, kv_len, block_size, dequant_scale):
+def gather_kv(cache_bits, kv_dtype, block_table_row, kv_len, block_size, dequant_scale,
+              token_scales=None):
     """Key/value rows 0..kv_len-1 of one sequence as float64 [kv_len, Hkv, D].
 
     Row j comes from block ``block_table_row[j // block_size]``, slot
     ``j % block_size`` (block-table indirection of the paged cache), decoded and
     multiplied by the per-tensor dequantisation scale (1 unless fp8).
+    ``token_scales``: optional per-token scales, float [num_blocks, block_size,
+    Hkv] indexed like the cache; row j of kv head g is further multiplied by
+    ``token_scales[page, slot, g]`` (AITER PR #3962, section "Testing" and the
+    review reply: per-token K and V scales, each with its own strides).
     """
     j = np.arange(kv_len)
     pages = np.asarray(block_table_row)[j // block_size]
     slots = j % block_size
     raw = cache_bits[pages, slots]
-    return float(dequant_scale) * decode(raw, kv_dtype)
+    rows = float(dequant_scale) * decode(raw, kv_dtype)
+    if token_scales is not None:
+        ts = np.asarray(token_scales)[pages, slots].astype(np.float64)  # [kv_len, Hkv]
+        rows = rows * ts[:, :, None]
+    return rows
 
 
 def visible_mask(pos, kv_len, window):
@@ -126,7 +137,8 @@ def row_attention(x, vis, V, sink):
 def attention(q, k_cache, v_cache, block_table, cu_seqlens_q, seq_lens, *,
               q_dtype, kv_dtype, block_size, scale, num_q_heads, num_kv_heads,
               window=0, softcap=0.0, alibi_slopes=None, sinks=None,
-              k_scale=1.0, v_scale=1.0, rows=None, qq_bias=None, **_unused):
+              k_scale=1.0, v_scale=1.0, k_token_scales=None, v_token_scales=None,
+              rows=None, qq_bias=None, **_unused):
     """Plain-definition attention in float64.
 
     q: stored bits [total_q, Hq, D]; k_cache/v_cache: stored bits
@@ -134,6 +146,7 @@ def attention(q, k_cache, v_cache, block_table, cu_seqlens_q, seq_lens, *,
     cu_seqlens_q int [num_seqs + 1]; seq_lens int [num_seqs].
     rows: optional sorted array of query-token indices to compute (default all).
     qq_bias: optional float [rows >= max q_len, stride] matrix (natural units).
+    k_token_scales / v_token_scales: optional float [num_blocks, block_size, Hkv].
     Returns (out [n_rows, Hq, D], lse [n_rows, Hq]) in float64, rows in the
     order of ``rows``.  lse includes the sink term; -inf where nothing is seen.
     """
@@ -151,8 +164,10 @@ def attention(q, k_cache, v_cache, block_table, cu_seqlens_q, seq_lens, *,
             continue
         kv_len = int(seq_lens[s])
         ctx = kv_len - (q1 - q0)
-        K = gather_kv(k_cache, kv_dtype, block_table[s], kv_len, block_size, k_scale)
-        V = gather_kv(v_cache, kv_dtype, block_table[s], kv_len, block_size, v_scale)
+        K = gather_kv(k_cache, kv_dtype, block_table[s], kv_len, block_size, k_scale,
+                      k_token_scales)
+        V = gather_kv(v_cache, kv_dtype, block_table[s], kv_len, block_size, v_scale,
+                      v_token_scales)
         rel = np.arange(kv_len) - ctx
         for c0 in range(0, len(sel), _ROW_CHUNK):
             idx = sel[c0:c0 + _ROW_CHUNK]

@@ -1,16 +1,17 @@
 """Pins of the CPU oracle against facts that do not come from the oracle itself.
 
 * format decoders: closed-form codes and library decoders (numpy float16, torch
-  bfloat16 / float8_e4m3fn) over every code;
-* the hand-worked examples in tests/golden/hand_example.json and
-  tests/golden/qq_bias_example.json;
+  bfloat16 / float8_e4m3fn / float8_e4m3fnuz) over every code;
+* the hand-worked examples in tests/golden/hand_example.json,
+  tests/golden/qq_bias_example.json and tests/golden/token_scales_example.json;
 * a brute-force loop implementation written independently below, on tiny
   random problems with every feature combination;
 * torch's float64 scaled_dot_product_attention for the dense special case
   (also with a QQ-bias passed as its additive float mask);
 * closed forms (all-zero keys, geometric ALiBi weights, two-key softcap) and
   invariants (window >= kv_len, window 1, block-table permutation, batching,
-  partition merge for any partition count).
+  partition merge for any partition count, per-token scales that are uniform
+  or scaled by a constant).
 """
 
 import json
@@ -24,7 +25,7 @@ import torch
 
 import oracle
 from oracle import attention, merge_partials_base2, partition_states_base2
-from oracle.formats import decode, decode_bf16, decode_e4m3fn, decode_fp16
+from oracle.formats import decode, decode_bf16, decode_e4m3fn, decode_e4m3fnuz, decode_fp16
 from synth import make_case
 
 GOLDEN = os.path.join(os.path.dirname(__file__), "golden", "hand_example.json")
@@ -79,12 +80,34 @@ def test_e4m3fn_closed_forms_and_torch():
     assert np.array_equal(ref[m], got[m])
 
 
-def test_e4m3_quantiser_roundtrip():
+def test_e4m3fnuz_closed_forms_and_torch():
+    assert decode_e4m3fnuz(0x40) == 1.0  # exponent 8 = bias
+    assert decode_e4m3fnuz(0x38) == 0.5
+    assert decode_e4m3fnuz(0x7F) == 240.0 and decode_e4m3fnuz(0xFF) == -240.0
+    assert decode_e4m3fnuz(0x78) == 128.0  # all-ones exponent is a normal
+    assert decode_e4m3fnuz(0x01) == 2.0 ** -10
+    assert decode_e4m3fnuz(0x08) == 2.0 ** -7
+    assert decode_e4m3fnuz(0x00) == 0.0
+    assert np.isnan(decode_e4m3fnuz(0x80))
+    codes = torch.arange(256, dtype=torch.uint8)
+    ref = codes.view(torch.float8_e4m3fnuz).to(torch.float64).numpy()
+    got = decode(codes.numpy(), "e4m3fnuz")
+    assert np.array_equal(np.isnan(got), np.isnan(ref))
+    fin = ~np.isnan(ref)
+    assert np.array_equal(got[fin], ref[fin])
+    # same bits, half the value, wherever both dialects are finite
+    fn = decode(codes.numpy(), "e4m3fn")
+    both = fin & ~np.isnan(fn)
+    assert np.array_equal(got[both], fn[both] / 2)
+
+
+@pytest.mark.parametrize("dialect", ["e4m3fn", "e4m3fnuz"])
+def test_e4m3_quantiser_roundtrip(dialect):
     """Every finite e4m3 value survives the generator's storage rounding unchanged."""
     from synth.workloads import _round_storage
-    vals = decode(np.arange(256, dtype=np.uint8), "e4m3fn")
+    vals = decode(np.arange(256, dtype=np.uint8), dialect)
     fin = np.isfinite(vals)
-    back = decode(_round_storage(vals[fin].astype(np.float32), "e4m3fn"), "e4m3fn")
+    back = decode(_round_storage(vals[fin].astype(np.float32), dialect), dialect)
     assert np.array_equal(back, vals[fin])
 
 
@@ -205,6 +228,66 @@ def test_qq_bias_hand_example():
     np.testing.assert_allclose(lse[:, 0], [_val(x) for x in g["lse"]], rtol=0, atol=1e-12)
 
 
+@pytest.mark.parametrize("dialect", ["e4m3fn", "e4m3fnuz"])
+def test_token_scales_hand_example(dialect):
+    g = json.load(open(os.path.join(os.path.dirname(GOLDEN), "token_scales_example.json")))
+    inp = g["inputs"]
+    codes = inp["codes"][dialect]
+    nb, bt = inp["num_blocks"], inp["block_table"]
+    kc = np.full((nb, 1, 1, 2), codes["nan"], dtype=np.uint8)
+    vc = np.full((nb, 1, 1, 2), codes["nan"], dtype=np.uint8)
+    kts = np.full((nb, 1, 1), np.nan)
+    vts = np.full((nb, 1, 1), np.nan)
+    for j, b in enumerate(bt):
+        kc[b, 0, 0] = codes["k"][j]
+        vc[b, 0, 0] = codes["v"][j]
+        kts[b, 0, 0] = inp["k_token_scales"][j]
+        vts[b, 0, 0] = inp["v_token_scales"][j]
+    q = _bits(np.array(inp["q"], dtype=np.float32)[None], "bf16")
+    o, lse = attention(q, kc, vc, np.array([bt], dtype=np.int32), np.array([0, 1]),
+                       np.array([2]), q_dtype="bf16", kv_dtype=dialect, block_size=1,
+                       scale=_val(inp["scale"]), num_q_heads=1, num_kv_heads=1,
+                       k_token_scales=kts, v_token_scales=vts)
+    np.testing.assert_allclose(o[0, 0], g["out"], rtol=0, atol=1e-12)
+    assert abs(lse[0, 0] - _val(g["lse"])) < 1e-12
+
+
+def _token_case(dialect, seed, **kw):
+    return make_case(seqs=[(3, 37), (1, 20), (5, 5)], head_dim=8, num_q_heads=4,
+                     num_kv_heads=2, block_size=4, q_dtype="bf16", kv_dtype=dialect,
+                     token_scales=True, seed=seed, **kw)
+
+
+@pytest.mark.parametrize("dialect", ["e4m3fn", "e4m3fnuz"])
+def test_uniform_token_scales_equal_a_tensor_scale(dialect):
+    c = _token_case(dialect, 11)
+    ks, vs = 0.375, 1.875  # exact in the float32 scale arrays
+    ref = attention(**dict(c, k_token_scales=None, v_token_scales=None, k_scale=ks,
+                           v_scale=vs))
+    got = attention(**dict(c, k_token_scales=np.full_like(c["k_token_scales"], ks),
+                           v_token_scales=np.full_like(c["v_token_scales"], vs)))
+    np.testing.assert_allclose(got[0], ref[0], rtol=0, atol=1e-13)
+    np.testing.assert_allclose(got[1], ref[1], rtol=0, atol=1e-13)
+
+
+@pytest.mark.parametrize("dialect", ["e4m3fn", "e4m3fnuz"])
+def test_token_scale_identities(dialect):
+    """Scaling every K token scale by c is scaling the softmax scale by c; scaling
+    every V token scale by c scales the output by c; a per-tensor factor multiplies
+    the per-token ones."""
+    c = _token_case(dialect, 12, sinks=True, window=9)
+    o, lse = attention(**c)
+    k2 = attention(**dict(c, k_token_scales=c["k_token_scales"] * 2.0))
+    s2 = attention(**dict(c, scale=c["scale"] * 2.0))
+    np.testing.assert_allclose(k2[0], s2[0], rtol=1e-12, atol=1e-13)
+    v2 = attention(**dict(c, v_token_scales=c["v_token_scales"] * 0.25))
+    np.testing.assert_allclose(v2[0], o * 0.25, rtol=1e-12, atol=1e-13)
+    np.testing.assert_allclose(v2[1], lse, rtol=0, atol=1e-13)
+    t2 = attention(**dict(c, k_scale=2.0, k_token_scales=c["k_token_scales"] / 2,
+                          v_scale=4.0, v_token_scales=c["v_token_scales"] / 4))
+    np.testing.assert_allclose(t2[0], o, rtol=1e-12, atol=1e-13)
+
+
 # ----------------------------------------------------------------------------- brute force
 
 def _dec_lib(bits, dtype):
@@ -214,7 +297,8 @@ def _dec_lib(bits, dtype):
         return b.view(np.float16).astype(np.float64)
     if dtype == "bf16":
         return torch.from_numpy(b.view(np.int16).copy()).view(torch.bfloat16).double().numpy()
-    return torch.from_numpy(b.copy()).view(torch.float8_e4m3fn).double().numpy()
+    fp8 = torch.float8_e4m3fn if dtype == "e4m3fn" else torch.float8_e4m3fnuz
+    return torch.from_numpy(b.copy()).view(fp8).double().numpy()
 
 
 def brute_force(c):
@@ -222,6 +306,8 @@ def brute_force(c):
     qf = _dec_lib(c["q"], c["q_dtype"])
     kf = _dec_lib(c["k_cache"], c["kv_dtype"]) * c.get("k_scale", 1.0)
     vf = _dec_lib(c["v_cache"], c["kv_dtype"]) * c.get("v_scale", 1.0)
+    kts = c.get("k_token_scales")
+    vts = c.get("v_token_scales")
     H, Hk = c["num_q_heads"], c["num_kv_heads"]
     D = qf.shape[2]
     bs = c["block_size"]
@@ -247,6 +333,8 @@ def brute_force(c):
                         continue
                     blk = c["block_table"][s][j // bs]
                     krow = kf[blk, j % bs, g]
+                    if kts is not None:
+                        krow = krow * float(kts[blk][j % bs][g])
                     x = c["scale"] * sum(qf[t, h, d] * krow[d] for d in range(D))
                     if cap > 0:
                         x = cap * math.tanh(x / cap)
@@ -255,7 +343,10 @@ def brute_force(c):
                     if qq is not None and j >= kv - ql:
                         x += float(qq[i][j - (kv - ql)])
                     logits.append(x)
-                    vals.append(vf[blk, j % bs, g])
+                    vrow = vf[blk, j % bs, g]
+                    if vts is not None:
+                        vrow = vrow * float(vts[blk][j % bs][g])
+                    vals.append(vrow)
                 if not logits:
                     continue
                 allx = logits + ([float(sinks[h])] if sinks is not None else [])
@@ -277,12 +368,17 @@ FEATURES = [
     dict(window=4, alibi=True),
     dict(qq_bias=24),
     dict(qq_bias=20, alibi=True, softcap=1.5, window=6),
+    dict(token_scales=True),
+    dict(token_scales=True, window=4, sinks=True),
 ]
 
 
 @pytest.mark.parametrize("fi", range(len(FEATURES)))
-@pytest.mark.parametrize("dtype,kvd", [("f16", "f16"), ("bf16", "bf16"), ("bf16", "e4m3fn")])
+@pytest.mark.parametrize("dtype,kvd", [("f16", "f16"), ("bf16", "bf16"), ("bf16", "e4m3fn"),
+                                       ("f16", "e4m3fnuz")])
 def test_oracle_matches_brute_force(fi, dtype, kvd):
+    if FEATURES[fi].get("token_scales") and not kvd.startswith("e4m3"):
+        pytest.skip("per-token scales exist only for fp8 caches")
     rng = np.random.default_rng(fi * 7 + len(dtype) + len(kvd))
     for trial in range(3):
         D = int(rng.choice([2, 4, 8]))
