@@ -34,11 +34,12 @@ HBM_PEAK_GBS = 8000.0
 MFMA_PEAK_TFLOPS = {"f16": 2500.0, "bf16": 2500.0}
 HEADLINE = "long_decode_bf16_d128_32q8kv_w4096"
 METRIC = "decode KV GB/s (% of HBM peak) + prefill TFLOP/s (% MFMA peak), 1 GPU"
-EB = {"f16": 2, "bf16": 2, "e4m3fn": 1}
+EB = {"f16": 2, "bf16": 2, "e4m3fn": 1, "e4m3fnuz": 1}
 
 
 def decode_bytes(case):
-    """Algorithmic bytes: attended K and V rows + Q read + O written."""
+    """Algorithmic bytes: attended K and V rows (+ their fp32 per-token K and V
+    scales when present) + Q read + O written."""
     D, Hk, Hq = case["head_dim"], case["num_kv_heads"], case["num_q_heads"]
     W = case["window"]
     kv = 0
@@ -51,6 +52,8 @@ def decode_bytes(case):
         first = (int(L) - ql - W + 1) if W > 0 else 0
         kv += int(L) - max(0, first)
     kvb = kv * Hk * D * EB[case["kv_dtype"]] * 2
+    if case.get("k_token_scales") is not None:
+        kvb += kv * Hk * 4 * 2
     tq = int(cu[-1])
     return kvb + tq * Hq * D * (EB[case["q_dtype"]] + EB[case["o_dtype"]])
 
@@ -87,7 +90,8 @@ class Runner:
             max_seqlen_k=case["max_seqlen_k"], scale=case["scale"], softcap=case["softcap"],
             window=case["window"], k_scale=case["k_scale"], v_scale=case["v_scale"],
             alibi_slopes=dev["alibi_slopes"], sinks=dev["sinks"], out=self.out,
-            qq_bias=dev.get("qq_bias"))
+            qq_bias=dev.get("qq_bias"), k_token_scales=dev.get("k_token_scales"),
+            v_token_scales=dev.get("v_token_scales"))
         self.force = {"auto": B.UA_PATH_AUTO, "2d": B.UA_PATH_2D, "splitkv": B.UA_PATH_SPLITKV}[path]
         self.n_part = n_part
         self.ncu = A.num_cus(dev["q"].device)
@@ -95,7 +99,9 @@ class Runner:
         self.args = A.make_args(dev["q"], dev["k_cache"], dev["v_cache"], dev["block_table"],
                                 dev["cu_seqlens_q"], dev["seq_lens"], self.out,
                                 alibi_slopes=dev["alibi_slopes"], sinks=dev["sinks"],
-                                qq_bias=dev.get("qq_bias"))
+                                qq_bias=dev.get("qq_bias"),
+                                k_token_scales=dev.get("k_token_scales"),
+                                v_token_scales=dev.get("v_token_scales"))
         nbytes = max(int(self.plan.workspace_bytes), 256)
         self.ws = torch.empty(nbytes, dtype=torch.uint8, device=dev["q"].device)
         self.ws_ptr = ctypes.c_void_p(self.ws.data_ptr())
@@ -399,7 +405,10 @@ def main():
                      "fp8kv_decode_b8_ctx6700_w4096",
                      "long_decode_bf16_d128_32q8kv_w4096_softcap_sinks",
                      "decode_64k_bf16_d128_32q8kv", "decode_mqa_bf16_d128_32q1kv",
-                     "decode_d256_fp16_16q2kv", "decode_fp16_d128_16q2kv_bs64"]:
+                     "decode_d256_fp16_16q2kv", "decode_fp16_d128_16q2kv_bs64",
+                     "fp8kv_pertoken_decode_b8_ctx6700_w4096",
+                     "fp8kv_fnuz_pertoken_decode_b8_ctx6700_w4096",
+                     "fp8kv_fnuz_decode_b32_ctx590"]:
             c = make_case(**WORKLOADS[name], poison=False)
             rr = time_case(c, args.steps, args.warmup, kernel_events=False)
             b = decode_bytes(c)
@@ -413,7 +422,8 @@ def main():
         for name in ["prefill_chunk1k_prefix8k_bf16", "prefill_chunk2k_prefix16k_bf16",
                      "prefill_4x1k_bf16", "prefill_8k_d256_24q4kv_bs784_bf16",
                      "d64_chunked_prefill_bf16_64q8kv_bs32_sinks_w128",
-                     "d64_prefill_bf16q_fp8kv_64q8kv_bs32_sinks"]:
+                     "d64_prefill_bf16q_fp8kv_64q8kv_bs32_sinks",
+                     "d64_prefill_bf16q_fnuz_pertoken_64q8kv_bs32_sinks"]:
             c = make_case(**WORKLOADS[name], poison=False)
             fl = prefill_flops(c)
             rr = time_case(c, max(5, args.steps // 5), 3, touched=decode_bytes(c),

@@ -12,13 +12,17 @@
  * query head h reads kv head h / (Hq / Hkv) (grouped-query attention).  Key j
  * is row (j % block_size) of cache block block_table[s][j / block_size].
  * The logit of key j is
- *     x = scale * <q, k_j>                    (k_j times k_scale for fp8 KV)
+ *     x = scale * <q, k_j>                    (k_j dequantised for fp8 KV, below)
  *     x = softcap * tanh(x / softcap)         if softcap > 0
  *     x = x + alibi_slopes[h] * (j - ctx)     if alibi_slopes != NULL
- * and the output row is sum_j softmax(x)_j * v_j (v_j times v_scale for fp8),
+ * and the output row is sum_j softmax(x)_j * v_j (v_j dequantised for fp8),
  * where an optional per-head sink logit sinks[h] joins the softmax
  * normaliser but has no value row (README section "Prefill-2D trace cohort").
  * A row that sees no key is written as zeros (AITER PR #3962 review reply).
+ * fp8 K/V (AITER PR #3962, section "Testing": both e4m3 dialects, per-tensor
+ * and per-token scales, K and V scales with their own strides): the stored
+ * code's value times k_scale (v_scale), times, when has_kv_token_scales, the
+ * fp32 per-token scale of the key's (block, slot, kv head).
  *
  * Two equivalent forms are offered (README "Why three tables"):
  *   ua_forward_2d      one pass: one workgroup per (query block, kv head);
@@ -53,9 +57,11 @@
 extern "C" {
 #endif
 
-#define UA_ABI_VERSION 2
+#define UA_ABI_VERSION 3
 
-typedef enum { UA_F16 = 0, UA_BF16 = 1, UA_FP8_E4M3FN = 2 } ua_dtype;
+/* UA_FP8_E4M3FN: OCP E4M3 (bias 7, max 448, no inf, NaN = S.1111.111).
+ * UA_FP8_E4M3FNUZ: E4M3 with bias 8 (max 240, no inf, no -0, NaN = 0x80). */
+typedef enum { UA_F16 = 0, UA_BF16 = 1, UA_FP8_E4M3FN = 2, UA_FP8_E4M3FNUZ = 3 } ua_dtype;
 
 typedef enum {
   UA_OK = 0,
@@ -81,7 +87,7 @@ typedef struct {
   int32_t max_seqlen_q;        /* upper bound of q_len over the batch */
   int32_t max_seqlen_k;        /* upper bound of kv_len over the batch */
   int32_t q_dtype;             /* ua_dtype: UA_F16 or UA_BF16 */
-  int32_t kv_dtype;            /* q_dtype, or UA_FP8_E4M3FN (OCP E4M3, finite) */
+  int32_t kv_dtype;            /* q_dtype, UA_FP8_E4M3FN or UA_FP8_E4M3FNUZ */
   int32_t o_dtype;             /* must equal q_dtype */
   float scale;                 /* logit scale, finite */
   float softcap;               /* <= 0: off */
@@ -103,6 +109,17 @@ typedef struct {
    * qq_bias_stride >= max_seqlen_q. */
   int32_t has_qq_bias;
   int32_t qq_bias_stride;
+  /* Per-token fp8 scales (AITER PR #3962, section "Testing" and review reply):
+   * when has_kv_token_scales (fp8 kv_dtype only), args->k_token_scales and
+   * args->v_token_scales are fp32 arrays; the key in slot t of block b, kv head
+   * g, is dequantised with k_token_scales[b * ks_stride_block + t *
+   * ks_stride_slot + g * ks_stride_head] (V likewise with the vs_ strides),
+   * multiplied with k_scale / v_scale.  Strides in elements, >= 0 (0
+   * broadcasts).  Entries of slots no sequence uses are never read. */
+  int32_t has_kv_token_scales;
+  int32_t reserved0;           /* must be 0 */
+  int64_t ks_stride_block, ks_stride_slot, ks_stride_head;
+  int64_t vs_stride_block, vs_stride_slot, vs_stride_head;
 } ua_problem;
 
 /* Output of ua_plan; treat as opaque except path, n_part and workspace_bytes. */
@@ -133,6 +150,9 @@ typedef struct {
                                   and has no sink), or NULL */
   const float* qq_bias;        /* [>= max_seqlen_q, qq_bias_stride] fp32 or NULL
                                   (must match has_qq_bias) */
+  const float* k_token_scales; /* per-token K scales or NULL (must match
+                                  has_kv_token_scales) */
+  const float* v_token_scales; /* per-token V scales or NULL (likewise) */
 } ua_args;
 
 /*

@@ -13,7 +13,8 @@ from . import binding as B
 
 _DT = {torch.float16: B.UA_F16, torch.bfloat16: B.UA_BF16}
 _KV_DT = {torch.float16: B.UA_F16, torch.bfloat16: B.UA_BF16,
-          torch.float8_e4m3fn: B.UA_FP8_E4M3FN, torch.uint8: B.UA_FP8_E4M3FN}
+          torch.float8_e4m3fn: B.UA_FP8_E4M3FN, torch.float8_e4m3fnuz: B.UA_FP8_E4M3FNUZ,
+          torch.uint8: B.UA_FP8_E4M3FN}
 _PATH = {"auto": B.UA_PATH_AUTO, "2d": B.UA_PATH_2D, "splitkv": B.UA_PATH_SPLITKV}
 
 _NUM_CUS = {}
@@ -30,10 +31,13 @@ def num_cus(device):
 
 def make_problem(q, k_cache, v_cache, block_table, *, num_seqs, max_seqlen_q, max_seqlen_k,
                  scale, softcap=0.0, window=0, k_scale=1.0, v_scale=1.0, alibi_slopes=None,
-                 sinks=None, out=None, qq_bias=None):
+                 sinks=None, out=None, qq_bias=None, k_token_scales=None,
+                 v_token_scales=None):
     """ua_problem for Q [total_q, Hq, D], caches [num_blocks, block_size, Hkv, D].
 
-    qq_bias: optional [rows, stride] fp32 matrix (row-contiguous)."""
+    qq_bias: optional [rows, stride] fp32 matrix (row-contiguous).
+    k_token_scales / v_token_scales: optional fp32 [num_blocks, block_size, Hkv]
+    per-token scales of an fp8 cache, any strides (passed through)."""
     total_q, Hq, D = q.shape
     nb, bs, Hkv, Dk = k_cache.shape
     if Dk != D or tuple(v_cache.shape) != tuple(k_cache.shape):
@@ -71,6 +75,15 @@ def make_problem(q, k_cache, v_cache, block_table, *, num_seqs, max_seqlen_q, ma
             raise ValueError("qq_bias needs at least max_seqlen_q rows")
         p.has_qq_bias = 1
         p.qq_bias_stride = qq_bias.stride(0)
+    if (k_token_scales is None) != (v_token_scales is None):
+        raise ValueError("give both per-token scale arrays or neither")
+    if k_token_scales is not None:
+        for t in (k_token_scales, v_token_scales):
+            if t.dtype != torch.float32 or tuple(t.shape) != (nb, bs, Hkv):
+                raise ValueError("per-token scales must be float32 [num_blocks, block_size, Hkv]")
+        p.has_kv_token_scales = 1
+        p.ks_stride_block, p.ks_stride_slot, p.ks_stride_head = k_token_scales.stride()
+        p.vs_stride_block, p.vs_stride_slot, p.vs_stride_head = v_token_scales.stride()
     p.q_stride_tok, p.q_stride_head = q.stride(0), q.stride(1)
     p.o_stride_tok, p.o_stride_head = o.stride(0), o.stride(1)
     p.kv_stride_block, p.kv_stride_slot, p.kv_stride_head = k_cache.stride()[:3]
@@ -78,7 +91,8 @@ def make_problem(q, k_cache, v_cache, block_table, *, num_seqs, max_seqlen_q, ma
 
 
 def make_args(q, k_cache, v_cache, block_table, cu_seqlens_q, seq_lens, out, lse=None,
-              alibi_slopes=None, sinks=None, qq_bias=None):
+              alibi_slopes=None, sinks=None, qq_bias=None, k_token_scales=None,
+              v_token_scales=None):
     for name, t, dt in (("block_table", block_table, torch.int32),
                         ("cu_seqlens_q", cu_seqlens_q, torch.int32),
                         ("seq_lens", seq_lens, torch.int32)):
@@ -98,6 +112,8 @@ def make_args(q, k_cache, v_cache, block_table, cu_seqlens_q, seq_lens, out, lse
     a.out = out.data_ptr()
     a.lse = lse.data_ptr() if lse is not None else None
     a.qq_bias = qq_bias.data_ptr() if qq_bias is not None else None
+    a.k_token_scales = k_token_scales.data_ptr() if k_token_scales is not None else None
+    a.v_token_scales = v_token_scales.data_ptr() if v_token_scales is not None else None
     return a
 
 
@@ -116,7 +132,7 @@ def workspace(nbytes, device, stream):
 def forward(q, k_cache, v_cache, block_table, cu_seqlens_q, seq_lens, *, max_seqlen_q,
             max_seqlen_k, scale, softcap=0.0, window=0, k_scale=1.0, v_scale=1.0,
             alibi_slopes=None, sinks=None, out=None, lse=None, path="auto", n_part=0,
-            ws=None, qq_bias=None):
+            ws=None, qq_bias=None, k_token_scales=None, v_token_scales=None):
     """Unified paged varlen attention; returns (out, plan).
 
     path: "auto" (dispatcher), "2d" (one pass) or "splitkv" (partitions + reduce).
@@ -130,10 +146,11 @@ def forward(q, k_cache, v_cache, block_table, cu_seqlens_q, seq_lens, *, max_seq
     prob = make_problem(q, k_cache, v_cache, block_table, num_seqs=num_seqs,
                         max_seqlen_q=max_seqlen_q, max_seqlen_k=max_seqlen_k, scale=scale,
                         softcap=softcap, window=window, k_scale=k_scale, v_scale=v_scale,
-                        alibi_slopes=alibi_slopes, sinks=sinks, out=out, qq_bias=qq_bias)
+                        alibi_slopes=alibi_slopes, sinks=sinks, out=out, qq_bias=qq_bias,
+                        k_token_scales=k_token_scales, v_token_scales=v_token_scales)
     plan = B.ua_plan(prob, num_cus(q.device), _PATH[path], n_part)
     args = make_args(q, k_cache, v_cache, block_table, cu_seqlens_q, seq_lens, out, lse,
-                     alibi_slopes, sinks, qq_bias)
+                     alibi_slopes, sinks, qq_bias, k_token_scales, v_token_scales)
     stream = torch.cuda.current_stream(q.device)
     sp = ctypes.c_void_p(stream.cuda_stream)
     if plan.path == B.UA_PATH_2D:

@@ -13,7 +13,7 @@ import threading
 HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libua.so")
 
-UA_F16, UA_BF16, UA_FP8_E4M3FN = 0, 1, 2
+UA_F16, UA_BF16, UA_FP8_E4M3FN, UA_FP8_E4M3FNUZ = 0, 1, 2, 3
 UA_PATH_AUTO, UA_PATH_2D, UA_PATH_SPLITKV = 0, 1, 2
 UA_OK = 0
 
@@ -40,6 +40,11 @@ class UaProblem(ctypes.Structure):
         ("kv_stride_block", ctypes.c_int64), ("kv_stride_slot", ctypes.c_int64),
         ("kv_stride_head", ctypes.c_int64),
         ("has_qq_bias", ctypes.c_int32), ("qq_bias_stride", ctypes.c_int32),
+        ("has_kv_token_scales", ctypes.c_int32), ("reserved0", ctypes.c_int32),
+        ("ks_stride_block", ctypes.c_int64), ("ks_stride_slot", ctypes.c_int64),
+        ("ks_stride_head", ctypes.c_int64),
+        ("vs_stride_block", ctypes.c_int64), ("vs_stride_slot", ctypes.c_int64),
+        ("vs_stride_head", ctypes.c_int64),
     ]
 
 
@@ -59,6 +64,7 @@ class UaArgs(ctypes.Structure):
         ("seq_lens", ctypes.c_void_p), ("alibi_slopes", ctypes.c_void_p),
         ("sinks", ctypes.c_void_p), ("out", ctypes.c_void_p), ("lse", ctypes.c_void_p),
         ("qq_bias", ctypes.c_void_p),
+        ("k_token_scales", ctypes.c_void_p), ("v_token_scales", ctypes.c_void_p),
     ]
 
 

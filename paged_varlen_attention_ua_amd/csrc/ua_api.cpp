@@ -41,13 +41,16 @@ uint64_t problem_hash(const ua_problem* p) {
   hs.add(p->has_alibi); hs.add(p->has_sinks); hs.add(p->q_stride_tok); hs.add(p->q_stride_head);
   hs.add(p->o_stride_tok); hs.add(p->o_stride_head); hs.add(p->kv_stride_block);
   hs.add(p->kv_stride_slot); hs.add(p->kv_stride_head); hs.add(p->has_qq_bias);
-  hs.add(p->qq_bias_stride);
+  hs.add(p->qq_bias_stride); hs.add(p->has_kv_token_scales);
+  hs.add(p->ks_stride_block); hs.add(p->ks_stride_slot); hs.add(p->ks_stride_head);
+  hs.add(p->vs_stride_block); hs.add(p->vs_stride_slot); hs.add(p->vs_stride_head);
   return hs.h;
 }
 
 int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
 bool is_16bit(int32_t t) { return t == UA_F16 || t == UA_BF16; }
+bool is_fp8(int32_t t) { return t == UA_FP8_E4M3FN || t == UA_FP8_E4M3FNUZ; }
 
 ua_status validate(const ua_problem* p) {
   if (!p) return UA_EINVAL;
@@ -63,12 +66,27 @@ ua_status validate(const ua_problem* p) {
   if (p->num_seqs > 0 && p->total_q > (int64_t)p->num_seqs * p->max_seqlen_q) return UA_EINVAL;
   if (!std::isfinite(p->scale) || !std::isfinite(p->softcap)) return UA_EINVAL;
   if (!is_16bit(p->q_dtype)) return UA_EUNSUPPORTED;
-  if (p->kv_dtype != p->q_dtype && p->kv_dtype != UA_FP8_E4M3FN) return UA_EUNSUPPORTED;
+  if (p->kv_dtype != p->q_dtype && !is_fp8(p->kv_dtype)) return UA_EUNSUPPORTED;
   if (p->o_dtype != p->q_dtype) return UA_EUNSUPPORTED;
-  if (p->kv_dtype == UA_FP8_E4M3FN) {
+  if (is_fp8(p->kv_dtype)) {
     if (!std::isfinite(p->k_scale) || !std::isfinite(p->v_scale) || p->k_scale <= 0.f ||
         p->v_scale <= 0.f)
       return UA_EINVAL;
+  }
+  if (p->reserved0 != 0) return UA_EINVAL;
+  if (p->has_kv_token_scales) {
+    if (!is_fp8(p->kv_dtype)) return UA_EUNSUPPORTED;
+    if (p->ks_stride_block < 0 || p->ks_stride_slot < 0 || p->ks_stride_head < 0 ||
+        p->vs_stride_block < 0 || p->vs_stride_slot < 0 || p->vs_stride_head < 0)
+      return UA_EINVAL;
+    // The kernels form (block, slot) offsets of the scale arrays in 32 bits.
+    const int64_t lim = (int64_t)1 << 31;
+    auto fits = [&](int64_t sb, int64_t ss) {
+      return sb < lim && ss < lim &&
+             std::max<int64_t>(p->num_blocks - 1, 0) * sb + (int64_t)(p->block_size - 1) * ss < lim;
+    };
+    if (!fits(p->ks_stride_block, p->ks_stride_slot) || !fits(p->vs_stride_block, p->vs_stride_slot))
+      return UA_EUNSUPPORTED;
   }
   if (p->head_dim != 64 && p->head_dim != 128 && p->head_dim != 256) return UA_EUNSUPPORTED;
   if ((int64_t)p->total_q * p->num_q_heads >= (int64_t)1 << 31) return UA_EUNSUPPORTED;
@@ -77,7 +95,7 @@ ua_status validate(const ua_problem* p) {
       p->kv_stride_head <= 0)
     return UA_EINVAL;
   // 16-byte vector access: strides in whole 16-byte units.
-  const int64_t kv_vec = p->kv_dtype == UA_FP8_E4M3FN ? 16 : 8;
+  const int64_t kv_vec = is_fp8(p->kv_dtype) ? 16 : 8;
   if (p->q_stride_tok % 8 || p->q_stride_head % 8 || p->o_stride_tok % 8 || p->o_stride_head % 8)
     return UA_EUNSUPPORTED;
   if (p->kv_stride_block % kv_vec || p->kv_stride_slot % kv_vec || p->kv_stride_head % kv_vec)
@@ -98,6 +116,9 @@ ua_status check_args(const ua_problem* p, const ua_args* a) {
   if ((p->has_alibi != 0) != (a->alibi_slopes != nullptr)) return UA_EINVAL;
   if ((p->has_sinks != 0) != (a->sinks != nullptr)) return UA_EINVAL;
   if ((p->has_qq_bias != 0) != (a->qq_bias != nullptr)) return UA_EINVAL;
+  if ((p->has_kv_token_scales != 0) != (a->k_token_scales != nullptr) ||
+      (p->has_kv_token_scales != 0) != (a->v_token_scales != nullptr))
+    return UA_EINVAL;
   auto aligned = [](const void* ptr, uintptr_t n) { return ((uintptr_t)ptr % n) == 0; };
   if (!aligned(a->q, 16) || !aligned(a->out, 16) || !aligned(a->k_cache, 16) ||
       !aligned(a->v_cache, 16))
@@ -128,6 +149,16 @@ Params make_params(const ua_problem* p, const ua_plan_t* plan, const ua_args* a,
   q.lse = a->lse;
   q.qq_bias = p->has_qq_bias ? a->qq_bias : nullptr;
   q.qq_stride = p->has_qq_bias ? p->qq_bias_stride : 0;
+  if (p->has_kv_token_scales) {
+    q.k_tscale = a->k_token_scales;
+    q.v_tscale = a->v_token_scales;
+    q.ks_stride_block = p->ks_stride_block;
+    q.ks_stride_slot = p->ks_stride_slot;
+    q.ks_stride_head = p->ks_stride_head;
+    q.vs_stride_block = p->vs_stride_block;
+    q.vs_stride_slot = p->vs_stride_slot;
+    q.vs_stride_head = p->vs_stride_head;
+  }
   if (ws) {
     const int64_t R = (int64_t)p->total_q * p->num_q_heads;
     char* base = reinterpret_cast<char*>(ws);
@@ -156,8 +187,10 @@ Params make_params(const ua_problem* p, const ua_plan_t* plan, const ua_args* a,
   int trips = 0;
   while ((1 << trips) < p->num_seqs + 1) ++trips;
   q.search_trips = trips;
-  const bool fp8 = p->kv_dtype == UA_FP8_E4M3FN;
-  const float ks = fp8 ? p->k_scale : 1.0f;
+  const bool fp8 = is_fp8(p->kv_dtype);
+  // e4m3fnuz codes are decoded to twice their value: halve both factors.
+  const double half = p->kv_dtype == UA_FP8_E4M3FNUZ ? 0.5 : 1.0;
+  const double ks = fp8 ? (double)p->k_scale * half : 1.0;
   const double log2e = 1.4426950408889634;
   q.qk_scale2 = (float)((double)p->scale * ks * log2e);
   q.softcap_on = p->softcap > 0.f ? 1 : 0;
@@ -165,7 +198,7 @@ Params make_params(const ua_problem* p, const ua_plan_t* plan, const ua_args* a,
     q.cap_in = (float)((double)p->scale * ks / p->softcap);
     q.cap_out2 = (float)((double)p->softcap * log2e);
   }
-  q.v_scale = fp8 ? p->v_scale : 1.0f;
+  q.v_scale = fp8 ? (float)((double)p->v_scale * half) : 1.0f;
   q.grid_x = plan->grid_x;
   q.seq_blocks = plan->flags & 1;
   return q;
@@ -220,7 +253,7 @@ ua_status ua_plan(const ua_problem* prob, int32_t num_cus, int32_t force_path,
   if (small && wgs > 0 && wgs < num_cus && eff_k > 1024) {
     // Measured on MI355X: about one small workgroup per CU for 16-bit KV and two
     // for fp8 KV (half the bytes per key), at least 256 keys per partition.
-    const int64_t per_cu = prob->kv_dtype == UA_FP8_E4M3FN ? 2 : 1;
+    const int64_t per_cu = is_fp8(prob->kv_dtype) ? 2 : 1;
     const int64_t want = ceil_div(per_cu * num_cus, wgs);
     const int64_t by_len = std::max<int64_t>(1, eff_k / 256);
     auto_parts = (int)std::max<int64_t>(1, std::min<int64_t>(std::min(want, by_len), 64));
@@ -282,11 +315,13 @@ static ua_status check_plan(const ua_problem* prob, const ua_plan_t* plan, int32
 static ua_status launch_main(const ua_problem* prob, const ua_plan_t* plan, const Params& q,
                              bool split, void* stream) {
   dim3 grid((unsigned)plan->grid_x, (unsigned)plan->grid_y, (unsigned)plan->grid_z);
-  const int fp8 = prob->kv_dtype == UA_FP8_E4M3FN;
+  const int fmt = prob->kv_dtype == UA_FP8_E4M3FN     ? kKvE4m3fn
+                  : prob->kv_dtype == UA_FP8_E4M3FNUZ ? kKvE4m3fnuz
+                                                      : kKv16;
   hipError_t e = plan->kernel == 0
-                     ? launch_small(q, prob->q_dtype, fp8, prob->head_dim, split, grid,
+                     ? launch_small(q, prob->q_dtype, fmt, prob->head_dim, split, grid,
                                     (hipStream_t)stream)
-                     : launch_large(q, prob->q_dtype, fp8, prob->head_dim, split, grid,
+                     : launch_large(q, prob->q_dtype, fmt, prob->head_dim, split, grid,
                                     (hipStream_t)stream);
   return e == hipSuccess ? UA_OK : UA_EHIP;
 }

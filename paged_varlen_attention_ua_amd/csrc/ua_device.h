@@ -16,6 +16,7 @@ typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
 
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
@@ -87,11 +88,31 @@ __device__ __forceinline__ float hi16(uint32_t v) {
   }
 }
 
-// Two OCP E4M3 codes (bytes 0,1 when hi == false, bytes 2,3 otherwise) -> packed QT pair.
-// Every E4M3 value is exactly representable in fp16 and bf16, so this is exact.
-template <int QT>
+// Byte permute: result byte i = byte sel_i of the 8-byte value {hi:lo}.
+__device__ __forceinline__ uint32_t perm_b32(uint32_t hi, uint32_t lo, uint32_t sel) {
+  return __builtin_amdgcn_perm(hi, lo, sel);
+}
+
+// Two E4M3 codes (bytes 0,1 when hi == false, bytes 2,3 otherwise) -> packed QT pair.
+// OCP e4m3fn (FNUZ == false): every value is exactly representable in fp16 and
+// bf16, so this is exact.
+// e4m3fnuz (FNUZ == true): the code of a value is the e4m3fn code of twice that
+// value, except for 0x7F / 0xFF (+-240, NaN in e4m3fn) and 0x80 (NaN; -0 in
+// e4m3fn, never produced by a quantiser).  The result is TWICE the fnuz value
+// (the caller folds the factor 1/2 into its fp32 scales): the magnitudes are
+// converted as e4m3fn, the NaN of 0x7F is clamped to 480 by an unsigned 16-bit
+// minimum (every finite e4m3fn magnitude is <= 448 < 480, and a non-negative
+// float orders like its bits), and the sign bits are put back.  Exact as well.
+template <int QT, bool FNUZ = false>
 __device__ __forceinline__ uint32_t fp8x2_to(uint32_t v, bool hi) {
-  if constexpr (QT == UA_F16) {
+  if constexpr (FNUZ) {
+    const uint32_t mag = fp8x2_to<QT, false>(v & 0x7F7F7F7Fu, hi);
+    const u16x2 cap = QT == UA_F16 ? u16x2{0x5F80, 0x5F80} : u16x2{0x43F0, 0x43F0};
+    const u16x2 m = __builtin_elementwise_min(__builtin_bit_cast(u16x2, mag), cap);
+    // sign of byte 0/2 -> bit 15, of byte 1/3 -> bit 31
+    const uint32_t sgn = perm_b32(0u, v, hi ? 0x030c020cu : 0x010c000cu) & 0x80008000u;
+    return __builtin_bit_cast(uint32_t, m) | sgn;
+  } else if constexpr (QT == UA_F16) {
     return __builtin_bit_cast(uint32_t,
                               hi ? __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(v, 1.0f, true)
                                  : __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(v, 1.0f, false));
@@ -103,19 +124,14 @@ __device__ __forceinline__ uint32_t fp8x2_to(uint32_t v, bool hi) {
 }
 
 // 8 E4M3 codes (2 dwords) -> 8 QT values (4 dwords), order preserved.
-template <int QT>
+template <int QT, bool FNUZ = false>
 __device__ __forceinline__ u32x4 fp8x8_to(u32x2 v) {
   u32x4 r;
-  r[0] = fp8x2_to<QT>(v[0], false);
-  r[1] = fp8x2_to<QT>(v[0], true);
-  r[2] = fp8x2_to<QT>(v[1], false);
-  r[3] = fp8x2_to<QT>(v[1], true);
+  r[0] = fp8x2_to<QT, FNUZ>(v[0], false);
+  r[1] = fp8x2_to<QT, FNUZ>(v[0], true);
+  r[2] = fp8x2_to<QT, FNUZ>(v[1], false);
+  r[3] = fp8x2_to<QT, FNUZ>(v[1], true);
   return r;
-}
-
-// Byte permute: result byte i = byte sel_i of the 8-byte value {hi:lo}.
-__device__ __forceinline__ uint32_t perm_b32(uint32_t hi, uint32_t lo, uint32_t sel) {
-  return __builtin_amdgcn_perm(hi, lo, sel);
 }
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }

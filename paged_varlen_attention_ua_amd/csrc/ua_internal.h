@@ -52,12 +52,19 @@ struct Params {
   void* out;
   float* lse;  // [total_q, Hq] or null
   const float* qq_bias;  // [>= max q_len, qq_stride] or null
+  // Per-token fp8 scales (or null): key in (block b, slot t) of kv head g is
+  // scaled by k_tscale[b * ks_stride_block + t * ks_stride_slot + g * ks_stride_head]
+  // (and likewise v_tscale), on top of the per-tensor factors below.
+  const float* k_tscale;
+  const float* v_tscale;
   float* ws_m;
   float* ws_l;
   float* ws_acc;
   int64_t q_stride_tok, q_stride_head;
   int64_t o_stride_tok, o_stride_head;
   int64_t kv_stride_block, kv_stride_slot, kv_stride_head;
+  int64_t ks_stride_block, ks_stride_slot, ks_stride_head;
+  int64_t vs_stride_block, vs_stride_slot, vs_stride_head;
   int32_t num_seqs, total_q, num_q_heads, num_kv_heads, group;
   int32_t block_size, max_blocks_per_seq;
   FastDiv bs_div;
@@ -65,20 +72,25 @@ struct Params {
   int32_t n_part;       // partitions (1 = one pass)
   int32_t window;       // <= 0: off
   int32_t search_trips; // ceil(log2(num_seqs + 1))
-  float qk_scale2;      // scale * k_scale * log2(e): raw dot -> base-2 logit
-  float cap_in;         // scale * k_scale / softcap (softcap on)
+  float qk_scale2;      // scale * kf * log2(e): raw dot -> base-2 logit
+  float cap_in;         // scale * kf / softcap (softcap on)
   float cap_out2;       // softcap * log2(e)
-  float v_scale;        // fp8 value scale (1 otherwise)
+  float v_scale;        // vf
+  // kf, vf: the per-tensor k_scale / v_scale for fp8 caches (1 otherwise),
+  // halved for e4m3fnuz, whose codes the kernels decode to twice their value.
   int32_t softcap_on;
   int32_t grid_x;       // number of query-block slots launched along x
   int32_t seq_blocks;   // 1: block x is the sequence index (every query run fits one block)
   int32_t qq_stride;    // QQ-bias row stride (elements)
 };
 
+// Storage format of the K/V cache as the kernels see it.
+enum KvFmt { kKv16 = 0, kKvE4m3fn = 1, kKvE4m3fnuz = 2 };
+
 // Launchers (defined next to their kernels).  Return hipError_t of the launch.
-hipError_t launch_small(const Params& p, int q_dtype, int kv_fp8, int head_dim, bool split,
+hipError_t launch_small(const Params& p, int q_dtype, int kv_fmt, int head_dim, bool split,
                         dim3 grid, hipStream_t stream);
-hipError_t launch_large(const Params& p, int q_dtype, int kv_fp8, int head_dim, bool split,
+hipError_t launch_large(const Params& p, int q_dtype, int kv_fmt, int head_dim, bool split,
                         dim3 grid, hipStream_t stream);
 hipError_t launch_reduce(const Params& p, int o_dtype, int head_dim, hipStream_t stream);
 

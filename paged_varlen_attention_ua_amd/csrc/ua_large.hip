@@ -24,7 +24,11 @@
 //     (the mask-phase split of the README's "BLOCK_M=128" section);
 //   * O^T = V^T P^T on 32x32x16 MFMA: P^T is already the B operand in the
 //     registers the S^T accumulator left it in, and V^T comes from
-//     ds_read_b64_tr_b16 transposed LDS reads (README "3D vs 3D").
+//     ds_read_b64_tr_b16 transposed LDS reads (README "3D vs 3D");
+//   * fp8 caches with per-token scales: the wave that looks up a tile's rows
+//     also loads the tile's K and V scales into a three-deep LDS ring; the K
+//     scale multiplies the raw dot product and the V scale the probability
+//     fed to the PV MFMA (the softmax sum keeps the unscaled probability).
 // Output: the final rows (one pass) or the partition's (m, l, acc) (split).
 
 #include <type_traits>
@@ -108,7 +112,13 @@ struct Stage {
   uint32_t v[FP8 ? LargeCfg<D>::CPT : 1][2];
 };
 
-template <int QT, bool FP8, int D, bool SPLIT>
+// Ring slots of the per-token scale buffer (one dummy slot without scales).
+template <bool ON>
+constexpr int tsc_lds() {
+  return ON ? 3 : 1;
+}
+
+template <int QT, bool FP8, int D, bool SPLIT, bool FNUZ, bool TS>
 __global__ __launch_bounds__(256, (D > 128 ? 1 : 2)) void large_kernel(Params p) {
   using C = LargeCfg<D>;
   constexpr int TK = C::TK;
@@ -120,6 +130,8 @@ __global__ __launch_bounds__(256, (D > 128 ? 1 : 2)) void large_kernel(Params p)
   __shared__ int64_t sTab0[TK];
   __shared__ int64_t sTab1[TK];
   __shared__ int32_t sm_pg[C::MAXPG];
+  // Per-token scales of tile t in ring slot t % 3: [slot][0: K, 1: V][key].
+  __shared__ __attribute__((aligned(16))) float sSc[tsc_lds<FP8 && TS>()][2][TK];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -230,6 +242,11 @@ __global__ __launch_bounds__(256, (D > 128 ? 1 : 2)) void large_kernel(Params p)
   // Row byte offsets (page * block stride + slot * slot stride) of keys
   // kt .. kt + TK - 1, each clamped into [kl, k1 - 1]: a key outside the range
   // reads a real row of the sequence (finite values) whose score is masked.
+  // With per-token scales the lane also loads its key's K and V scales into
+  // sc_k / sc_v (offsets fit 32 bits: host check); store_sc puts them in the
+  // ring once they have arrived.
+  constexpr bool tsc = FP8 && TS;
+  float sc_k = 0.0f, sc_v = 0.0f;
   auto fill_tab = [&](int64_t* tab, int kt) __attribute__((always_inline)) {
     if (lane < TK) {
       const int key = min(max(kt + lane, kl), k1 - 1);
@@ -238,6 +255,21 @@ __global__ __launch_bounds__(256, (D > 128 ? 1 : 2)) void large_kernel(Params p)
       const int j = (int)bi - pg_first;
       const int32_t page = j < C::MAXPG ? sm_pg[j] : bt_row[bi];
       tab[lane] = (int64_t)page * blk_b + (int64_t)slot * slot_b;
+      if constexpr (tsc) {
+        sc_k = p.k_tscale[(int64_t)kvh * p.ks_stride_head +
+                          (page * (int32_t)p.ks_stride_block + slot * (int32_t)p.ks_stride_slot)];
+        sc_v = p.v_tscale[(int64_t)kvh * p.vs_stride_head +
+                          (page * (int32_t)p.vs_stride_block + slot * (int32_t)p.vs_stride_slot)];
+      }
+    }
+  };
+  auto store_sc = [&](int tile) __attribute__((always_inline)) {
+    if constexpr (tsc) {
+      if (lane < TK) {
+        float* dst = &sSc[tile % 3][0][0];
+        dst[lane] = sc_k;
+        dst[TK + lane] = sc_v;
+      }
     }
   };
 
@@ -288,8 +320,8 @@ __global__ __launch_bounds__(256, (D > 128 ? 1 : 2)) void large_kernel(Params p)
         const int i = tid + 256 * u;
         const int r = i / C::NC;
         const int at = r * ROWB + 16 * ((i % C::NC) ^ swz<D>(r));
-        *reinterpret_cast<u32x4*>(dk + at) = fp8x8_to<QT>(u32x2{st.k[u][0], st.k[u][1]});
-        *reinterpret_cast<u32x4*>(dv + at) = fp8x8_to<QT>(u32x2{st.v[u][0], st.v[u][1]});
+        *reinterpret_cast<u32x4*>(dk + at) = fp8x8_to<QT, FNUZ>(u32x2{st.k[u][0], st.k[u][1]});
+        *reinterpret_cast<u32x4*>(dv + at) = fp8x8_to<QT, FNUZ>(u32x2{st.v[u][0], st.v[u][1]});
       }
     }
   };
@@ -320,7 +352,8 @@ __global__ __launch_bounds__(256, (D > 128 ? 1 : 2)) void large_kernel(Params p)
 
   const int ntiles = (k1 - k0 + TK - 1) / TK;
 
-  auto compute = [&](const char* sk, const char* sv, int kt) __attribute__((always_inline)) {
+  auto compute = [&](const char* sk, const char* sv, int kt, const float* sc)
+      __attribute__((always_inline)) {
     // ---- S^T = K Q^T
     f32x16 sacc[C::KB];
 #pragma unroll
@@ -331,6 +364,18 @@ __global__ __launch_bounds__(256, (D > 128 ? 1 : 2)) void large_kernel(Params p)
         const u32x4 a = *reinterpret_cast<const u32x4*>(sk + 32 * kb * ROWB + kaddr[c]);
         sacc[kb] = mfma32<QT>(a, qop[c], sacc[kb]);
       }
+    }
+    // Per-token K scales: registers 4j .. 4j + 3 of block kb are keys
+    // 32 kb + 8 j + 4 g2 + 0..3 of the tile.
+    if constexpr (tsc) {
+#pragma unroll
+      for (int kb = 0; kb < C::KB; ++kb)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const f32x4 k4 = *reinterpret_cast<const f32x4*>(sc + 32 * kb + 8 * j + 4 * g2);
+#pragma unroll
+          for (int i = 0; i < 4; ++i) sacc[kb][4 * j + i] *= k4[i];
+        }
     }
     // ---- logits and masks.  Without softcap/ALiBi the raw dot products are
     // kept (cs = scale * log2 e is applied in the FMA feeding exp2); with them
@@ -417,13 +462,22 @@ __global__ __launch_bounds__(256, (D > 128 ? 1 : 2)) void large_kernel(Params p)
     float psum = 0.0f;
 #pragma unroll
     for (int kk = 0; kk < TK / 16; ++kk) {
+      // V scales of this operand's keys 16 kk + 4 g2 + {0..3, 8..11} (q = 0..3).
+      f32x4 v4[2] = {f32x4{1.f, 1.f, 1.f, 1.f}, f32x4{1.f, 1.f, 1.f, 1.f}};
+      if constexpr (tsc) {
+        v4[0] = *reinterpret_cast<const f32x4*>(sc + TK + 16 * kk + 4 * g2);
+        v4[1] = *reinterpret_cast<const f32x4*>(sc + TK + 16 * kk + 4 * g2 + 8);
+      }
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
         const float a = fast_exp2(__builtin_fmaf(sacc[kk >> 1][8 * (kk & 1) + 2 * q], cs, -m_use));
         const float b =
             fast_exp2(__builtin_fmaf(sacc[kk >> 1][8 * (kk & 1) + 2 * q + 1], cs, -m_use));
         psum += a + b;
-        pop[kk][q] = pack2<QT>(a, b);
+        if constexpr (tsc)
+          pop[kk][q] = pack2<QT>(a * v4[q >> 1][2 * (q & 1)], b * v4[q >> 1][2 * (q & 1) + 1]);
+        else
+          pop[kk][q] = pack2<QT>(a, b);
       }
     }
     l_run += psum;
@@ -439,9 +493,15 @@ __global__ __launch_bounds__(256, (D > 128 ? 1 : 2)) void large_kernel(Params p)
     }
   };
 
-  // Prologue: tables of tiles 0 and 1, then tile 0 into buffer 0.
-  if (wave == 0) fill_tab(sTab0, k0);
-  if (wave == 1 && ntiles > 1) fill_tab(sTab1, k0 + TK);
+  // Prologue: tables (and scales) of tiles 0 and 1, then tile 0 into buffer 0.
+  if (wave == 0) {
+    fill_tab(sTab0, k0);
+    store_sc(0);
+  }
+  if (wave == 1 && ntiles > 1) {
+    fill_tab(sTab1, k0 + TK);
+    store_sc(1);
+  }
   __syncthreads();
   if constexpr (FP8) {
     stage_load(sTab0);
@@ -471,14 +531,16 @@ __global__ __launch_bounds__(256, (D > 128 ? 1 : 2)) void large_kernel(Params p)
       else
         issue_copy(nxt_k, nxt_v, tab_next);
     }
-    if (t + 2 < ntiles && wave == (t & 3)) fill_tab(tab_fill, kt + 2 * TK);
-    if (wave_live) compute(cur_k, cur_v, kt);
+    const bool filler = t + 2 < ntiles && wave == (t & 3);
+    if (filler) fill_tab(tab_fill, kt + 2 * TK);
+    if (wave_live) compute(cur_k, cur_v, kt, &sSc[tsc ? t % 3 : 0][0][0]);
     if (more) {
       if constexpr (FP8)
         stage_store(nxt_k, nxt_v);
       else
         wait_vmem();
     }
+    if (filler) store_sc(t + 2);
     __syncthreads();
   };
   for (int t = 0; t < ntiles; t += 2) {
@@ -527,35 +589,49 @@ __global__ __launch_bounds__(256, (D > 128 ? 1 : 2)) void large_kernel(Params p)
   }
 }
 
-template <int QT, bool FP8, int D>
+template <int QT, bool FP8, int D, bool FNUZ, bool TS>
 hipError_t launch_large_t(const Params& p, bool split, dim3 grid, hipStream_t stream) {
   if (split)
-    hipLaunchKernelGGL((large_kernel<QT, FP8, D, true>), grid, dim3(256), 0, stream, p);
+    hipLaunchKernelGGL((large_kernel<QT, FP8, D, true, FNUZ, TS>), grid, dim3(256), 0, stream, p);
   else
-    hipLaunchKernelGGL((large_kernel<QT, FP8, D, false>), grid, dim3(256), 0, stream, p);
+    hipLaunchKernelGGL((large_kernel<QT, FP8, D, false, FNUZ, TS>), grid, dim3(256), 0, stream, p);
   return hipGetLastError();
 }
 
-template <int QT, bool FP8>
+template <int QT, bool FP8, bool FNUZ, bool TS>
 hipError_t launch_large_d(const Params& p, int head_dim, bool split, dim3 grid,
                           hipStream_t stream) {
   switch (head_dim) {
-    case 64: return launch_large_t<QT, FP8, 64>(p, split, grid, stream);
-    case 128: return launch_large_t<QT, FP8, 128>(p, split, grid, stream);
-    case 256: return launch_large_t<QT, FP8, 256>(p, split, grid, stream);
+    case 64: return launch_large_t<QT, FP8, 64, FNUZ, TS>(p, split, grid, stream);
+    case 128: return launch_large_t<QT, FP8, 128, FNUZ, TS>(p, split, grid, stream);
+    case 256: return launch_large_t<QT, FP8, 256, FNUZ, TS>(p, split, grid, stream);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+// Per-token scales are a template switch: kernels without them are unchanged.
+template <int QT>
+hipError_t launch_large_q(const Params& p, int kv_fmt, int head_dim, bool split, dim3 grid,
+                          hipStream_t stream) {
+  const bool ts = p.k_tscale != nullptr;
+  switch (kv_fmt) {
+    case kKv16: return launch_large_d<QT, false, false, false>(p, head_dim, split, grid, stream);
+    case kKvE4m3fn:
+      return ts ? launch_large_d<QT, true, false, true>(p, head_dim, split, grid, stream)
+                : launch_large_d<QT, true, false, false>(p, head_dim, split, grid, stream);
+    case kKvE4m3fnuz:
+      return ts ? launch_large_d<QT, true, true, true>(p, head_dim, split, grid, stream)
+                : launch_large_d<QT, true, true, false>(p, head_dim, split, grid, stream);
     default: return hipErrorInvalidValue;
   }
 }
 
 }  // namespace
 
-hipError_t launch_large(const Params& p, int q_dtype, int kv_fp8, int head_dim, bool split,
+hipError_t launch_large(const Params& p, int q_dtype, int kv_fmt, int head_dim, bool split,
                         dim3 grid, hipStream_t stream) {
-  if (q_dtype == UA_F16)
-    return kv_fp8 ? launch_large_d<UA_F16, true>(p, head_dim, split, grid, stream)
-                  : launch_large_d<UA_F16, false>(p, head_dim, split, grid, stream);
-  return kv_fp8 ? launch_large_d<UA_BF16, true>(p, head_dim, split, grid, stream)
-                : launch_large_d<UA_BF16, false>(p, head_dim, split, grid, stream);
+  return q_dtype == UA_F16 ? launch_large_q<UA_F16>(p, kv_fmt, head_dim, split, grid, stream)
+                           : launch_large_q<UA_BF16>(p, kv_fmt, head_dim, split, grid, stream);
 }
 
 }  // namespace ua

@@ -29,6 +29,11 @@
 //     two deep: the next tile's loads are in flight while a tile is computed.
 //   * Logits are kept in the base-2 domain (pre-multiplied by log2 e, exp2 for
 //     the exponentials), the README's convention (section "2D vs 2D").
+//   * fp8 caches with per-token scales: each lane loads one scale per tile (K
+//     or V, of a key whose score its own 16-lane row holds) and ds_bpermute
+//     hands the scales to the lanes that need them; the K scale multiplies the
+//     raw dot product, the V scale the probability fed to the PV MFMA (the
+//     softmax sum keeps the unscaled probability).
 
 #include "ua_device.h"
 
@@ -88,6 +93,7 @@ struct Tile {
   using C = SmallCfg<QT, FP8, D>;
   uint32_t k[2][C::KW];
   uint32_t v[8][C::VW];
+  float sc;  // per-token scale loaded by this lane (fp8 with per-token scales)
 };
 
 // K row piece of one lane (`row` = byte address of the key's head row).
@@ -207,11 +213,11 @@ __device__ __forceinline__ void load_tile_any(Tile<QT, FP8, D>& t, const Params&
 }
 
 // A operand of the c-th QK MFMA for key half hb.
-template <int QT, bool FP8, int D>
+template <int QT, bool FP8, int D, bool FNUZ>
 __device__ __forceinline__ u32x4 k_operand(const Tile<QT, FP8, D>& t, int hb, int c) {
   if constexpr (FP8) {
     u32x2 raw = {t.k[hb][2 * c], t.k[hb][2 * c + 1]};
-    return fp8x8_to<QT>(raw);
+    return fp8x8_to<QT, FNUZ>(raw);
   } else {
     u32x4 r = {t.k[hb][4 * c], t.k[hb][4 * c + 1], t.k[hb][4 * c + 2], t.k[hb][4 * c + 3]};
     return r;
@@ -221,7 +227,7 @@ __device__ __forceinline__ u32x4 k_operand(const Tile<QT, FP8, D>& t, int hb, in
 // A operand of the c-th PV MFMA (O^T = V^T P^T).  Lane l supplies
 // V[key_j][E*(l%16) + c] for its eight keys j (j < 4: 4j + g, else
 // 16 + 4(j - 4) + g: the keys its S^T accumulator holds), two keys per dword.
-template <int QT, bool FP8, int D>
+template <int QT, bool FP8, int D, bool FNUZ>
 __device__ __forceinline__ u32x4 v_operand(const Tile<QT, FP8, D>& t, int c) {
   u32x4 op;
   if constexpr (!FP8) {
@@ -234,12 +240,18 @@ __device__ __forceinline__ u32x4 v_operand(const Tile<QT, FP8, D>& t, int c) {
     const uint32_t sel = bc | ((bc + 4) << 8) | 0x0c0c0000u;
 #pragma unroll
     for (int q = 0; q < 4; ++q)
-      op[q] = fp8x2_to<QT>(perm_b32(t.v[2 * q + 1][c >> 2], t.v[2 * q][c >> 2], sel), false);
+      op[q] = fp8x2_to<QT, FNUZ>(perm_b32(t.v[2 * q + 1][c >> 2], t.v[2 * q][c >> 2], sel),
+                                 false);
   }
   return op;
 }
 
-template <int QT, bool FP8, int D, bool SPLIT, bool PAGE16>
+// Float handed from lane src to this lane (ds_bpermute; byte address 4 src).
+__device__ __forceinline__ float lane_get(float v, int src) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_ds_bpermute(4 * src, __builtin_bit_cast(int, v)));
+}
+
+template <int QT, bool FP8, int D, bool SPLIT, bool PAGE16, bool FNUZ, bool TS>
 __global__ __launch_bounds__(64 * kSmallWaves, 2) void small_kernel(Params p) {
   using C = SmallCfg<QT, FP8, D>;
   constexpr int E = C::E;
@@ -349,6 +361,35 @@ __global__ __launch_bounds__(64 * kSmallWaves, 2) void small_kernel(Params p) {
 #pragma unroll
   for (int jj = 0; jj < 4; ++jj) v_lane[jj] = (4 * jj + g) * slot_b32 + C::E * r16 * C::EB;
 
+  // Per-token scales (fp8 only): lane (g, r16) loads the scale of tile key
+  // 16 hb + 4 r + g, hb = (r16 / 4) % 2, r = r16 % 4, from the K scales
+  // (r16 < 8) or the V scales (r16 >= 8).  Offsets fit 32 bits (host check).
+  constexpr bool tsc = FP8 && TS;
+  const int sc_key = 16 * ((r16 >> 2) & 1) + 4 * (r16 & 3) + g;
+  const float* sc_base = nullptr;
+  int32_t sc_sb = 0, sc_ss = 0;
+  if constexpr (tsc) {
+    const bool kside = r16 < 8;
+    sc_base = kside ? p.k_tscale + kvh * p.ks_stride_head : p.v_tscale + kvh * p.vs_stride_head;
+    sc_sb = (int32_t)(kside ? p.ks_stride_block : p.vs_stride_block);
+    sc_ss = (int32_t)(kside ? p.ks_stride_slot : p.vs_stride_slot);
+  }
+  // Scale of tile key kt + sc_key, clamped into the loadable range [kl, k1) of
+  // the partition (a clamped key is masked; its scale is a real, finite one).
+  // page2: the tile's two half-tile blocks (block_size % 16 == 0), else null.
+  auto load_scale = [&](Tile<QT, FP8, D>& t, int kt, const int32_t* page2)
+      __attribute__((always_inline)) {
+    if constexpr (tsc) {
+      {
+        const int key = min(max(kt + sc_key, kl), k1 - 1);
+        const uint32_t bi = fastdiv((uint32_t)key, p.bs_div);
+        const int slot = key - (int)bi * p.block_size;
+        const int32_t pg = page2 != nullptr ? (key - kt < 16 ? page2[0] : page2[1]) : bt_row[bi];
+        t.sc = sc_base[pg * sc_sb + slot * sc_ss];
+      }
+    }
+  };
+
   auto tile_pages = [&](int i, int32_t* page) __attribute__((always_inline)) {
     if (i < kPreTiles) {
       page[0] = __builtin_amdgcn_readfirstlane(sm_pg[wave][2 * i]);
@@ -365,8 +406,10 @@ __global__ __launch_bounds__(64 * kSmallWaves, 2) void small_kernel(Params p) {
       int32_t page[2];
       tile_pages(i, page);
       load_tile_paged16<QT, FP8, D>(t, p, kbase, vbase, kt, page, kl, k1, g, r16);
+      load_scale(t, kt, page);
     } else {
       load_tile_any<QT, FP8, D>(t, p, bt_row, kbase, vbase, kt, kl, k1, g, r16);
+      load_scale(t, kt, nullptr);
     }
   };
   // Interior tile (PAGE16 only): all 32 keys loadable.
@@ -374,6 +417,7 @@ __global__ __launch_bounds__(64 * kSmallWaves, 2) void small_kernel(Params p) {
     int32_t page[2];
     tile_pages(i, page);
     load_tile_fast<QT, FP8, D>(t, p, kbase, vbase, wk0 + kStride * i, page, k_lane, v_lane);
+    load_scale(t, wk0 + kStride * i, page);
   };
 
   f32x4 oacc[E];
@@ -388,7 +432,14 @@ __global__ __launch_bounds__(64 * kSmallWaves, 2) void small_kernel(Params p) {
     for (int hb = 0; hb < 2; ++hb) {
       sacc[hb] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int c = 0; c < QC; ++c) sacc[hb] = mfma16<QT>(k_operand(t, hb, c), qop[c], sacc[hb]);
+      for (int c = 0; c < QC; ++c)
+        sacc[hb] = mfma16<QT>(k_operand<QT, FP8, D, FNUZ>(t, hb, c), qop[c], sacc[hb]);
+    }
+    // Per-token K scales of this lane's eight keys (from lanes 16 g + 4 hb + r).
+    float ksc[8];
+    if constexpr (tsc) {
+#pragma unroll
+      for (int j = 0; j < 8; ++j) ksc[j] = lane_get(t.sc, 16 * g + j);
     }
     float x[8];
 #pragma unroll
@@ -396,7 +447,8 @@ __global__ __launch_bounds__(64 * kSmallWaves, 2) void small_kernel(Params p) {
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int key = kt + 16 * hb + 4 * r + g;
-        const float raw = sacc[hb][r];
+        float raw = sacc[hb][r];
+        if constexpr (tsc) raw *= ksc[4 * hb + r];
         float v = p.softcap_on ? p.cap_out2 * tanh_fast(raw * p.cap_in) : raw * p.qk_scale2;
         x[4 * hb + r] = v + slope2 * (float)(key - ctx);
       }
@@ -433,17 +485,31 @@ __global__ __launch_bounds__(64 * kSmallWaves, 2) void small_kernel(Params p) {
     m_run = m_new;
     u32x4 pb;
     float psum = 0.0f;
+    if constexpr (tsc) {
+      // The PV weights carry the V scales (from lanes 16 g + 8 + 4 hb + r); the
+      // softmax sum does not.
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const uint32_t pk = pack2<QT>(fast_exp2(x[2 * q] - m_use), fast_exp2(x[2 * q + 1] - m_use));
-      pb[q] = pk;
-      psum += lo16<QT>(pk) + hi16<QT>(pk);
+      for (int q = 0; q < 4; ++q) {
+        const float e0 = fast_exp2(x[2 * q] - m_use), e1 = fast_exp2(x[2 * q + 1] - m_use);
+        pb[q] = pack2<QT>(e0 * lane_get(t.sc, 16 * g + 8 + 2 * q),
+                          e1 * lane_get(t.sc, 16 * g + 9 + 2 * q));
+        psum += e0 + e1;
+      }
+    } else {
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const uint32_t pk =
+            pack2<QT>(fast_exp2(x[2 * q] - m_use), fast_exp2(x[2 * q + 1] - m_use));
+        pb[q] = pk;
+        psum += lo16<QT>(pk) + hi16<QT>(pk);
+      }
     }
     l_run = l_run * alpha + psum;
 #pragma unroll
     for (int c = 0; c < E; ++c) oacc[c] *= alpha;
 #pragma unroll
-    for (int c = 0; c < E; ++c) oacc[c] = mfma16<QT>(v_operand(t, c), pb, oacc[c]);
+    for (int c = 0; c < E; ++c)
+      oacc[c] = mfma16<QT>(v_operand<QT, FP8, D, FNUZ>(t, c), pb, oacc[c]);
   };
 
   // One tile per wave in flight; latency is hidden by running three waves per
@@ -626,43 +692,58 @@ __global__ __launch_bounds__(64 * kSmallWaves, 2) void small_kernel(Params p) {
   }
 }
 
-template <int QT, bool FP8, int D>
+template <int QT, bool FP8, int D, bool FNUZ, bool TS>
 hipError_t launch_small_t(const Params& p, bool split, dim3 grid, hipStream_t stream) {
   const bool page16 = (p.block_size % 16) == 0;
+  const dim3 block(64 * kSmallWaves);
   if (split) {
     if (page16)
-      hipLaunchKernelGGL((small_kernel<QT, FP8, D, true, true>), grid, dim3(64 * kSmallWaves), 0, stream, p);
+      hipLaunchKernelGGL((small_kernel<QT, FP8, D, true, true, FNUZ, TS>), grid, block, 0, stream, p);
     else
-      hipLaunchKernelGGL((small_kernel<QT, FP8, D, true, false>), grid, dim3(64 * kSmallWaves), 0, stream, p);
+      hipLaunchKernelGGL((small_kernel<QT, FP8, D, true, false, FNUZ, TS>), grid, block, 0, stream, p);
   } else {
     if (page16)
-      hipLaunchKernelGGL((small_kernel<QT, FP8, D, false, true>), grid, dim3(64 * kSmallWaves), 0, stream, p);
+      hipLaunchKernelGGL((small_kernel<QT, FP8, D, false, true, FNUZ, TS>), grid, block, 0, stream, p);
     else
-      hipLaunchKernelGGL((small_kernel<QT, FP8, D, false, false>), grid, dim3(64 * kSmallWaves), 0, stream, p);
+      hipLaunchKernelGGL((small_kernel<QT, FP8, D, false, false, FNUZ, TS>), grid, block, 0, stream, p);
   }
   return hipGetLastError();
 }
 
-template <int QT, bool FP8>
+template <int QT, bool FP8, bool FNUZ, bool TS>
 hipError_t launch_small_d(const Params& p, int head_dim, bool split, dim3 grid,
                           hipStream_t stream) {
   switch (head_dim) {
-    case 64: return launch_small_t<QT, FP8, 64>(p, split, grid, stream);
-    case 128: return launch_small_t<QT, FP8, 128>(p, split, grid, stream);
-    case 256: return launch_small_t<QT, FP8, 256>(p, split, grid, stream);
+    case 64: return launch_small_t<QT, FP8, 64, FNUZ, TS>(p, split, grid, stream);
+    case 128: return launch_small_t<QT, FP8, 128, FNUZ, TS>(p, split, grid, stream);
+    case 256: return launch_small_t<QT, FP8, 256, FNUZ, TS>(p, split, grid, stream);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+// Per-token scales are a template switch: kernels without them are unchanged.
+template <int QT>
+hipError_t launch_small_q(const Params& p, int kv_fmt, int head_dim, bool split, dim3 grid,
+                          hipStream_t stream) {
+  const bool ts = p.k_tscale != nullptr;
+  switch (kv_fmt) {
+    case kKv16: return launch_small_d<QT, false, false, false>(p, head_dim, split, grid, stream);
+    case kKvE4m3fn:
+      return ts ? launch_small_d<QT, true, false, true>(p, head_dim, split, grid, stream)
+                : launch_small_d<QT, true, false, false>(p, head_dim, split, grid, stream);
+    case kKvE4m3fnuz:
+      return ts ? launch_small_d<QT, true, true, true>(p, head_dim, split, grid, stream)
+                : launch_small_d<QT, true, true, false>(p, head_dim, split, grid, stream);
     default: return hipErrorInvalidValue;
   }
 }
 
 }  // namespace
 
-hipError_t launch_small(const Params& p, int q_dtype, int kv_fp8, int head_dim, bool split,
+hipError_t launch_small(const Params& p, int q_dtype, int kv_fmt, int head_dim, bool split,
                         dim3 grid, hipStream_t stream) {
-  if (q_dtype == UA_F16)
-    return kv_fp8 ? launch_small_d<UA_F16, true>(p, head_dim, split, grid, stream)
-                  : launch_small_d<UA_F16, false>(p, head_dim, split, grid, stream);
-  return kv_fp8 ? launch_small_d<UA_BF16, true>(p, head_dim, split, grid, stream)
-                : launch_small_d<UA_BF16, false>(p, head_dim, split, grid, stream);
+  return q_dtype == UA_F16 ? launch_small_q<UA_F16>(p, kv_fmt, head_dim, split, grid, stream)
+                           : launch_small_q<UA_BF16>(p, kv_fmt, head_dim, split, grid, stream);
 }
 
 }  // namespace ua

@@ -63,6 +63,15 @@ DEC_D256 = dict(seqs=[(1, 1024), (1, 2048)], head_dim=256, num_q_heads=16, num_k
                 block_size=16, q_dtype="f16", seed=205)
 DEC_B64 = dict(C1, block_size=64, seed=206)
 
+# fp8 variants AITER PR #3962 tests (section "Testing": both e4m3 dialects,
+# per-tensor and per-token scales): the sliding-window fp8 decode shapes with
+# per-token K/V scales (K and V scale arrays laid out differently), in e4m3fn
+# and e4m3fnuz, and the d64 fp8 prefill with per-token e4m3fnuz scales.
+C4B_TOK = dict(C4B, token_scales=True, seed=124)
+C4B_FNUZ_TOK = dict(C4B, kv_dtype="e4m3fnuz", token_scales=True, seed=134)
+C4A_FNUZ = dict(C4A, kv_dtype="e4m3fnuz", seed=144)
+D64_FNUZ_TOK = dict(D64_FP8, kv_dtype="e4m3fnuz", token_scales=True, seed=212)
+
 WORKLOADS = {
     "decode_fp16_d128_16q2kv": C1,
     "mixed_fp16_d128_16q2kv": C2,
@@ -82,6 +91,10 @@ WORKLOADS = {
     "decode_mqa_bf16_d128_32q1kv": DEC_MQA,
     "decode_d256_fp16_16q2kv": DEC_D256,
     "decode_fp16_d128_16q2kv_bs64": DEC_B64,
+    "fp8kv_pertoken_decode_b8_ctx6700_w4096": C4B_TOK,
+    "fp8kv_fnuz_pertoken_decode_b8_ctx6700_w4096": C4B_FNUZ_TOK,
+    "fp8kv_fnuz_decode_b32_ctx590": C4A_FNUZ,
+    "d64_prefill_bf16q_fnuz_pertoken_64q8kv_bs32_sinks": D64_FNUZ_TOK,
 }
 
 NEXT_DECODE_WORKLOADS = [
@@ -89,10 +102,14 @@ NEXT_DECODE_WORKLOADS = [
     "decode_mqa_bf16_d128_32q1kv",
     "decode_d256_fp16_16q2kv",
     "decode_fp16_d128_16q2kv_bs64",
+    "fp8kv_pertoken_decode_b8_ctx6700_w4096",
+    "fp8kv_fnuz_pertoken_decode_b8_ctx6700_w4096",
+    "fp8kv_fnuz_decode_b32_ctx590",
 ]
 NEXT_PREFILL_WORKLOADS = [
     "d64_chunked_prefill_bf16_64q8kv_bs32_sinks_w128",
     "d64_prefill_bf16q_fp8kv_64q8kv_bs32_sinks",
+    "d64_prefill_bf16q_fnuz_pertoken_64q8kv_bs32_sinks",
 ]
 
 DECODE_WORKLOADS = [

@@ -2,7 +2,7 @@
 run it through the C ABI, compare with the oracle.
 
 Tolerances (max-abs against the float64 oracle; fp8 KV against the oracle on
-the dequantised cache): fp16 2e-3, bf16 1e-2, fp8 KV 2e-2.  Each element may
+the dequantised cache, either e4m3 dialect): fp16 2e-3, bf16 1e-2, fp8 KV 2e-2.  Each element may
 additionally differ by half a unit in the last place of the output type at the
 oracle's value: that is the error of rounding the exact result once to the
 output type, which no kernel can avoid (bf16 half-ULP is 7.8e-3 on [2, 4)).
@@ -13,12 +13,13 @@ import math
 import numpy as np
 import torch
 
-TOL = {"f16": 2e-3, "bf16": 1e-2, "e4m3fn": 2e-2}
+TOL = {"f16": 2e-3, "bf16": 1e-2, "e4m3fn": 2e-2, "e4m3fnuz": 2e-2}
 _MANT = {"f16": 10, "bf16": 7}
 
 
 def tolerance(case):
-    return TOL["e4m3fn"] if case["kv_dtype"] == "e4m3fn" else TOL[case["q_dtype"]]
+    kvd = case["kv_dtype"]
+    return TOL[kvd] if kvd.startswith("e4m3") else TOL[case["q_dtype"]]
 
 
 def half_ulp(ref, o_dtype):
@@ -34,7 +35,17 @@ def _torch_bits(arr, dtype, device):
         return t.view(torch.int16).view(torch.float16).to(device)
     if dtype == "bf16":
         return t.view(torch.int16).view(torch.bfloat16).to(device)
-    return t.view(torch.uint8).view(torch.float8_e4m3fn).to(device)
+    fp8 = torch.float8_e4m3fn if dtype == "e4m3fn" else torch.float8_e4m3fnuz
+    return t.view(torch.uint8).view(fp8).to(device)
+
+
+def _scales(arr, device):
+    """Per-token scales with their numpy strides kept (a transposed view stays one)."""
+    if arr is None:
+        return None
+    t = torch.from_numpy(arr).to(device)
+    assert t.stride() == tuple(s // 4 for s in arr.strides)
+    return t
 
 
 def to_device(case, device="cuda"):
@@ -51,6 +62,8 @@ def to_device(case, device="cuda"):
                else torch.from_numpy(np.asarray(case["sinks"], np.float32)).to(device)),
         qq_bias=(None if case.get("qq_bias") is None
                  else torch.from_numpy(np.asarray(case["qq_bias"], np.float32)).to(device)),
+        k_token_scales=_scales(case.get("k_token_scales"), device),
+        v_token_scales=_scales(case.get("v_token_scales"), device),
     )
     return d
 
@@ -74,7 +87,9 @@ def run(case, dev=None, path="auto", n_part=0, lse=False, poison_out=True, ws=No
                         scale=case["scale"], softcap=case["softcap"], window=case["window"],
                         k_scale=case["k_scale"], v_scale=case["v_scale"],
                         alibi_slopes=dev["alibi_slopes"], sinks=dev["sinks"], out=out,
-                        lse=lse_t, path=path, n_part=n_part, ws=ws, qq_bias=dev.get("qq_bias"))
+                        lse=lse_t, path=path, n_part=n_part, ws=ws, qq_bias=dev.get("qq_bias"),
+                        k_token_scales=dev.get("k_token_scales"),
+                        v_token_scales=dev.get("v_token_scales"))
     torch.cuda.synchronize()
     res = o.float().cpu().numpy().astype(np.float64)
     l = lse_t.cpu().numpy().astype(np.float64) if lse_t is not None else None

@@ -33,15 +33,16 @@ def test_library_exports_every_declared_symbol():
     lib = ctypes.CDLL(B.LIB_PATH)
     for fn in _declared_functions():
         assert hasattr(lib, fn), fn
-    assert U.ua_abi_version() == 2
+    assert U.ua_abi_version() == 3
 
 
 def test_struct_sizes_match_header_layout():
     # ua_problem: 6 int32, int64, 3 int32, 3 int32, 2 float, int32, 2 float, 2 int32, pad,
-    # 7 int64, 2 int32 (QQ-bias)
-    assert ctypes.sizeof(B.UaProblem) == 152
+    # 7 int64, 2 int32 (QQ-bias), 2 int32 + 6 int64 (per-token scales)
+    assert ctypes.sizeof(B.UaProblem) == 208
+    assert B.UaProblem.ks_stride_block.offset == 160
     assert ctypes.sizeof(B.UaPlan) == 48
-    assert ctypes.sizeof(B.UaArgs) == 88
+    assert ctypes.sizeof(B.UaArgs) == 104
 
 
 def problem(**kw):
@@ -124,10 +125,36 @@ def test_grid_covers_every_query_block():
     (dict(total_q=9), -1),
     (dict(has_qq_bias=1, qq_bias_stride=0), -1),
     (dict(max_seqlen_q=300, total_q=8, has_qq_bias=1, qq_bias_stride=256), -1),
+    (dict(has_kv_token_scales=1), -2),  # bf16 cache: per-token scales need fp8
+    (dict(kv_dtype=B.UA_FP8_E4M3FNUZ, kv_stride_block=16 * 8 * 128, has_kv_token_scales=1,
+          ks_stride_slot=-1), -1),
+    (dict(kv_dtype=B.UA_FP8_E4M3FNUZ, kv_stride_block=16 * 8 * 128, has_kv_token_scales=1,
+          vs_stride_block=1 << 22), -2),  # block offsets past 32 bits
+    (dict(reserved0=1), -1),
+    (dict(kv_dtype=B.UA_FP8_E4M3FNUZ, k_scale=float("nan")), -1),
 ])
 def test_invalid_problems_are_rejected(kw, code):
     st, _ = status_of(problem(**kw))
     assert st == code
+
+
+def test_fp8_dialects_and_per_token_scales_plan():
+    for kvd in (B.UA_FP8_E4M3FN, B.UA_FP8_E4M3FNUZ):
+        st, plan = status_of(problem(kv_dtype=kvd, kv_stride_block=16 * 8 * 128))
+        assert st == 0 and plan.n_part == 8
+        p = problem(kv_dtype=kvd, kv_stride_block=16 * 8 * 128, has_kv_token_scales=1,
+                    ks_stride_block=8 * 16, ks_stride_slot=1, ks_stride_head=16,
+                    vs_stride_block=16 * 8, vs_stride_slot=8, vs_stride_head=1)
+        st, plan2 = status_of(p)
+        assert st == 0 and plan2.n_part == 8
+        assert plan2.problem_hash != plan.problem_hash
+        # per-token arrays missing from the call
+        args = B.UaArgs()
+        for f in ("q", "k_cache", "v_cache", "block_table", "cu_seqlens_q", "seq_lens", "out"):
+            setattr(args, f, 1 << 20)
+        assert B.lib().ua_forward_splitkv(ctypes.byref(p), ctypes.byref(plan2),
+                                          ctypes.byref(args), ctypes.c_void_p(1 << 21),
+                                          1 << 30, None) == -1
 
 
 def test_forward_rejects_mismatched_plan_and_missing_workspace():

@@ -14,6 +14,7 @@ import torch
 
 import oracle
 from synth import WORKLOADS, make_case
+from synth.configs import NEXT_DECODE_WORKLOADS, NEXT_PREFILL_WORKLOADS
 from tests.gpu_common import (check_lse, compare, run, sample_rows, to_device, tolerance)
 
 pytestmark = pytest.mark.gpu
@@ -74,10 +75,8 @@ def test_prefill_full_size_sampled_rows(name, path, n_part):
     print(f"[ok] {name} path={plan.path} max_abs={err:.3e}", flush=True)
 
 
-NEXT_DECODE = ["decode_64k_bf16_d128_32q8kv", "decode_mqa_bf16_d128_32q1kv",
-               "decode_d256_fp16_16q2kv", "decode_fp16_d128_16q2kv_bs64"]
-NEXT_PREFILL = ["d64_chunked_prefill_bf16_64q8kv_bs32_sinks_w128",
-                "d64_prefill_bf16q_fp8kv_64q8kv_bs32_sinks"]
+NEXT_DECODE = NEXT_DECODE_WORKLOADS
+NEXT_PREFILL = NEXT_PREFILL_WORKLOADS
 
 
 @pytest.mark.parametrize("path,n_part", [("auto", 0), ("2d", 0), ("splitkv", 4)])
@@ -146,12 +145,66 @@ def test_block_sizes(bs, path, n_part):
 
 @pytest.mark.parametrize("D", [64, 128, 256])
 @pytest.mark.parametrize("dt,kvd", [("f16", "f16"), ("bf16", "bf16"), ("bf16", "e4m3fn"),
-                                     ("f16", "e4m3fn")])
+                                     ("f16", "e4m3fn"), ("bf16", "e4m3fnuz"),
+                                     ("f16", "e4m3fnuz")])
 def test_head_dims_and_dtypes(D, dt, kvd):
     case = make_case(seqs=MIXED_SEQS, seed=30 + D, **dict(BASE, head_dim=D, q_dtype=dt,
                                                            kv_dtype=kvd))
     _check(case, "auto", 0, label=f"D{D}-{dt}-{kvd}")
     _check(case, "splitkv", 3, label=f"D{D}-{dt}-{kvd}-split")
+
+
+# Decode-shaped batch (q_len * G <= 16: the small-block kernel).
+DECODE_SEQS = [(1, 300), (2, 90), (0, 12), (1, 1), (1, 700), (2, 33), (1, 1500)]
+
+
+@pytest.mark.parametrize("bs", [13, 16, 32])
+@pytest.mark.parametrize("shape", ["decode", "mixed"])
+@pytest.mark.parametrize("kvd", ["e4m3fn", "e4m3fnuz"])
+def test_per_token_scales(kvd, shape, bs):
+    """Per-token K/V scales (K and V arrays with different strides), both dialects,
+    both kernels, paged (bs 16, 32) and unaligned (bs 13) block sizes; scales of
+    unused slots are NaN."""
+    seqs = DECODE_SEQS if shape == "decode" else MIXED_SEQS
+    case = make_case(seqs=seqs, seed=60 + bs + len(kvd), token_scales=True,
+                     **dict(BASE, block_size=bs, kv_dtype=kvd))
+    assert case["k_token_scales"].strides != case["v_token_scales"].strides
+    for path, n_part in [("2d", 0), ("splitkv", 3), ("auto", 0)]:
+        _, plan = _check(case, path, n_part, label=f"{kvd}-{shape}-bs{bs}-{path}{n_part}")
+        assert plan.kernel == (0 if shape == "decode" else 1)
+
+
+@pytest.mark.parametrize("D", [64, 256])
+@pytest.mark.parametrize("kvd", ["e4m3fn", "e4m3fnuz"])
+def test_per_token_scales_head_dims(kvd, D):
+    for seqs, name in [(DECODE_SEQS, "decode"), (MIXED_SEQS, "mixed")]:
+        case = make_case(seqs=seqs, seed=70 + D, token_scales=True,
+                         **dict(BASE, head_dim=D, kv_dtype=kvd, q_dtype="f16"))
+        _check(case, "auto", 0, label=f"{kvd}-D{D}-{name}")
+        _check(case, "splitkv", 2, label=f"{kvd}-D{D}-{name}-split")
+
+
+@pytest.mark.parametrize("kvd", ["e4m3fn", "e4m3fnuz"])
+def test_per_token_scales_with_features(kvd):
+    """Window, sinks, softcap, ALiBi and QQ-bias together with per-token scales."""
+    for seqs in (DECODE_SEQS, [(1, 4), (3, 6), (2, 300), (5, 60), (64, 200)]):
+        for kw in [dict(window=17, sinks=True), dict(softcap=3.0, alibi=True),
+                   dict(qq_bias=128, window=40)]:
+            case = make_case(seqs=seqs, seed=80, token_scales=True,
+                             **dict(BASE, kv_dtype=kvd), **kw)
+            _check(case, "2d", 0, label=f"{kvd}-{kw}")
+            _check(case, "splitkv", 4, label=f"{kvd}-{kw}-split")
+
+
+def test_per_token_tile_ring_lengths():
+    """Large-kernel scale ring (three slots, filled two tiles ahead) over partitions
+    of 1 .. 6 tiles and a window that starts mid-tile."""
+    for kv, w in [(64, 0), (128, 0), (192, 0), (380, 0), (700, 150)]:
+        case = make_case(seqs=[(40, kv), (64, kv + 3)], seed=90 + kv, token_scales=True,
+                         window=w, **dict(BASE, kv_dtype="e4m3fnuz"))
+        for n_part in (1, 2, 3):
+            path = "2d" if n_part == 1 else "splitkv"
+            _check(case, path, n_part, label=f"kv{kv}-w{w}-p{n_part}")
 
 
 @pytest.mark.parametrize("Hq,Hkv", [(4, 4), (6, 2), (24, 4), (32, 2), (8, 1)])
