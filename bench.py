@@ -35,6 +35,7 @@ MFMA_PEAK_TFLOPS = {"f16": 2500.0, "bf16": 2500.0}
 HEADLINE = "long_decode_bf16_d128_32q8kv_w4096"
 METRIC = "decode KV GB/s (% of HBM peak) + prefill TFLOP/s (% MFMA peak), 1 GPU"
 EB = {"f16": 2, "bf16": 2, "e4m3fn": 1, "e4m3fnuz": 1}
+KERNEL_NAMES = {0: "small", 1: "large (128-row blocks)", 2: "large (256-row blocks)"}
 
 
 def decode_bytes(case):
@@ -433,7 +434,7 @@ def main():
                          "pct_mfma_peak": round(100 * tf / MFMA_PEAK_TFLOPS["bf16"], 2),
                          "ms_per_step": round(rr["ms_per_step"], 4),
                          "path": "splitkv" if rr["path"] == 2 else "2d",
-                         "kernel": "large" if rr["kernel"] == 1 else "small"}
+                         "kernel": KERNEL_NAMES[rr["kernel"]]}
         line["prefill"] = pre
         lat = {}
         for name in ["mixed_fp16_d128_16q2kv", "mixed_fp16_d128_16q2kv_alibi",
@@ -443,7 +444,7 @@ def main():
             lat[name] = {"us_per_step": round(rr["ms_per_step"] * 1e3, 2),
                          "TFLOP/s": round(prefill_flops(c) / (rr["ms_per_step"] * 1e-3) / 1e12, 2),
                          "path": "splitkv" if rr["path"] == 2 else "2d",
-                         "kernel": "large" if rr["kernel"] == 1 else "small"}
+                         "kernel": KERNEL_NAMES[rr["kernel"]]}
         line["latency_bound"] = lat
     if not args.no_cpu:
         line["cpu_baseline"] = cpu_baseline(make_case(**WORKLOADS[HEADLINE]))

@@ -125,7 +125,8 @@ typedef struct {
 /* Output of ua_plan; treat as opaque except path, n_part and workspace_bytes. */
 typedef struct {
   int32_t path;             /* UA_PATH_2D or UA_PATH_SPLITKV, never AUTO */
-  int32_t kernel;           /* 0: small query blocks (<= 16 rows), 1: large (MFMA prefill) */
+  int32_t kernel;           /* 0: small query blocks (<= 16 rows), 1: large (128 rows,
+                               MFMA prefill), 2: large with 256 rows (head_dim <= 128) */
   int32_t block_q;          /* query tokens per query block */
   int32_t n_part;           /* key-range partitions per query block (1 for 2D) */
   int32_t grid_x, grid_y, grid_z;

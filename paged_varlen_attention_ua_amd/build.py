@@ -13,7 +13,16 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 OUT = os.path.join(HERE, "libua.so")
 BUILD_DIR = os.path.join(HERE, "_build")
-SOURCES = ["ua_api.cpp", "ua_small.hip", "ua_large.hip", "ua_reduce.hip"]
+# (source, object, extra flags): the two kernel files are compiled once per
+# query dtype (UA_QT) so their instantiations build in parallel.
+SOURCES = [
+    ("ua_api.cpp", "ua_api.o", []),
+    ("ua_small.hip", "ua_small_f16.o", ["-DUA_QT=0"]),
+    ("ua_small.hip", "ua_small_bf16.o", ["-DUA_QT=1"]),
+    ("ua_large.hip", "ua_large_f16.o", ["-DUA_QT=0"]),
+    ("ua_large.hip", "ua_large_bf16.o", ["-DUA_QT=1"]),
+    ("ua_reduce.hip", "ua_reduce.o", []),
+]
 ARCH = "gfx950"
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
@@ -25,10 +34,11 @@ COMMON = [
 ]
 
 
-def _compile(src):
-    obj = os.path.join(BUILD_DIR, os.path.splitext(src)[0] + ".o")
+def _compile(entry):
+    src, obj_name, extra = entry
+    obj = os.path.join(BUILD_DIR, obj_name)
     lang = ["-x", "hip"] if src.endswith(".cpp") else []
-    cmd = [HIPCC, *COMMON, *lang, "-c", os.path.join(CSRC, src), "-o", obj]
+    cmd = [HIPCC, *COMMON, *extra, *lang, "-c", os.path.join(CSRC, src), "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"hipcc failed for {src}:\n{r.stdout}\n{r.stderr}")

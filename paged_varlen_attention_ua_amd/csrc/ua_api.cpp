@@ -235,15 +235,24 @@ ua_status ua_plan(const ua_problem* prob, int32_t num_cus, int32_t force_path,
   std::memset(plan, 0, sizeof(*plan));
   const int G = prob->num_q_heads / prob->num_kv_heads;
   // Small blocks (<= 16 rows, bandwidth-shaped) when every sequence's query
-  // run fits one of them; large MFMA blocks (128 rows) otherwise.
+  // run fits one of them; large MFMA blocks otherwise: 256 rows (eight waves,
+  // half the K/V reads per flop, a four-deep copy ring) for 16-bit caches with
+  // D <= 128 when some sequence fills one and blocks walk >= 4096 keys
+  // (measured on MI355X: a few % faster there; slower on shorter ranges and
+  // for fp8 caches, where two independent four-wave groups per CU overlap
+  // better), else 128 rows.
   const bool small = G <= kSmallRows && (int64_t)prob->max_seqlen_q * G <= kSmallRows;
-  plan->kernel = small ? 0 : 1;
-  plan->block_q = small ? kSmallRows / G : kLargeRows / G;
+  int64_t eff_k = prob->max_seqlen_k;
+  if (prob->window > 0)
+    eff_k = std::min<int64_t>(eff_k, (int64_t)prob->window + prob->max_seqlen_q - 1);
+  const bool eight = !small && prob->head_dim <= 128 && is_16bit(prob->kv_dtype) &&
+                     (int64_t)prob->max_seqlen_q * G >= kLarge8Rows && eff_k >= 4096;
+  plan->kernel = small ? 0 : (eight ? 2 : 1);
+  plan->block_q = small ? kSmallRows / G : (eight ? kLarge8Rows : kLargeRows) / G;
   const int bq = plan->block_q;
   const int64_t slots = prob->num_seqs > 0 ? (int64_t)prob->total_q / bq + prob->num_seqs : 0;
   const int64_t est_blocks =
       std::min<int64_t>(slots, (int64_t)prob->num_seqs * ceil_div(prob->max_seqlen_q, bq));
-  int64_t eff_k = prob->max_seqlen_k;
   if (prob->window > 0) eff_k = std::min<int64_t>(eff_k, (int64_t)prob->window + bq - 1);
   const int64_t wgs = est_blocks * prob->num_kv_heads;
 
@@ -257,13 +266,14 @@ ua_status ua_plan(const ua_problem* prob, int32_t num_cus, int32_t force_path,
     const int64_t want = ceil_div(per_cu * num_cus, wgs);
     const int64_t by_len = std::max<int64_t>(1, eff_k / 256);
     auto_parts = (int)std::max<int64_t>(1, std::min<int64_t>(std::min(want, by_len), 64));
-  } else if (!small && wgs > 0 && wgs < 2ll * num_cus && eff_k >= 1024) {
-    // Large blocks run two per CU: split a grid that does not fill that,
-    // keeping at least 512 keys per partition (256 and up to 64 partitions
-    // when at most half of a block's rows are live, e.g. decode with G > 16:
-    // there the key walk is bandwidth-shaped like the small blocks').
+  } else if (!small && wgs > 0 && wgs < (eight ? 1ll : 2ll) * num_cus && eff_k >= 1024) {
+    // Four-wave large blocks run two per CU, eight-wave ones one: split a grid
+    // that does not fill that, keeping at least 512 keys per partition (256
+    // and up to 64 partitions when at most half of a block's rows are live,
+    // e.g. decode with G > 16: there the key walk is bandwidth-shaped like the
+    // small blocks').
     const bool sparse_rows = (int64_t)std::min(prob->max_seqlen_q, bq) * G * 2 <= kLargeRows;
-    const int64_t want = ceil_div(2ll * num_cus, wgs);
+    const int64_t want = ceil_div((eight ? 1ll : 2ll) * num_cus, wgs);
     const int64_t by_len = std::max<int64_t>(1, eff_k / (sparse_rows ? 256 : 512));
     auto_parts = (int)std::max<int64_t>(
         1, std::min<int64_t>(std::min(want, by_len), sparse_rows ? 64 : 16));
@@ -308,7 +318,8 @@ static ua_status check_plan(const ua_problem* prob, const ua_plan_t* plan, int32
   ua_status st = validate(prob);
   if (st != UA_OK) return st;
   if (plan->problem_hash != problem_hash(prob) || plan->path != path) return UA_EPLAN;
-  if (plan->n_part < 1 || plan->block_q < 1) return UA_EPLAN;
+  if (plan->n_part < 1 || plan->block_q < 1 || plan->kernel < 0 || plan->kernel > 2)
+    return UA_EPLAN;
   return UA_OK;
 }
 
@@ -321,8 +332,8 @@ static ua_status launch_main(const ua_problem* prob, const ua_plan_t* plan, cons
   hipError_t e = plan->kernel == 0
                      ? launch_small(q, prob->q_dtype, fmt, prob->head_dim, split, grid,
                                     (hipStream_t)stream)
-                     : launch_large(q, prob->q_dtype, fmt, prob->head_dim, split, grid,
-                                    (hipStream_t)stream);
+                     : launch_large(q, prob->q_dtype, fmt, prob->head_dim, split,
+                                    plan->kernel == 2, grid, (hipStream_t)stream);
   return e == hipSuccess ? UA_OK : UA_EHIP;
 }
 

@@ -10,9 +10,9 @@ namespace ua {
 
 // Largest query group a small-block kernel packs into its 16 MFMA rows.
 constexpr int kSmallRows = 16;
-// Rows of a large (prefill) query block and its waves.
+// Rows of a large (prefill) query block: 32 per wave, four or eight waves.
 constexpr int kLargeRows = 128;
-constexpr int kLargeWaves = 4;
+constexpr int kLarge8Rows = 256;
 // Keys per inner tile of the small-block kernel (two 16-key MFMA blocks).
 constexpr int kSmallTile = 32;
 // Keys per inner tile of the large-block kernel.
@@ -87,11 +87,28 @@ struct Params {
 // Storage format of the K/V cache as the kernels see it.
 enum KvFmt { kKv16 = 0, kKvE4m3fn = 1, kKvE4m3fnuz = 2 };
 
-// Launchers (defined next to their kernels).  Return hipError_t of the launch.
-hipError_t launch_small(const Params& p, int q_dtype, int kv_fmt, int head_dim, bool split,
-                        dim3 grid, hipStream_t stream);
-hipError_t launch_large(const Params& p, int q_dtype, int kv_fmt, int head_dim, bool split,
-                        dim3 grid, hipStream_t stream);
+// Launchers (defined next to their kernels, one per query dtype).  Return
+// hipError_t of the launch.
+hipError_t launch_small_f16(const Params& p, int kv_fmt, int head_dim, bool split, dim3 grid,
+                            hipStream_t stream);
+hipError_t launch_small_bf16(const Params& p, int kv_fmt, int head_dim, bool split, dim3 grid,
+                             hipStream_t stream);
+hipError_t launch_large_f16(const Params& p, int kv_fmt, int head_dim, bool split,
+                            bool eight_waves, dim3 grid, hipStream_t stream);
+hipError_t launch_large_bf16(const Params& p, int kv_fmt, int head_dim, bool split,
+                             bool eight_waves, dim3 grid, hipStream_t stream);
+
+inline hipError_t launch_small(const Params& p, int q_dtype, int kv_fmt, int head_dim,
+                               bool split, dim3 grid, hipStream_t stream) {
+  return q_dtype == UA_F16 ? launch_small_f16(p, kv_fmt, head_dim, split, grid, stream)
+                           : launch_small_bf16(p, kv_fmt, head_dim, split, grid, stream);
+}
+inline hipError_t launch_large(const Params& p, int q_dtype, int kv_fmt, int head_dim,
+                               bool split, bool eight_waves, dim3 grid, hipStream_t stream) {
+  return q_dtype == UA_F16
+             ? launch_large_f16(p, kv_fmt, head_dim, split, eight_waves, grid, stream)
+             : launch_large_bf16(p, kv_fmt, head_dim, split, eight_waves, grid, stream);
+}
 hipError_t launch_reduce(const Params& p, int o_dtype, int head_dim, hipStream_t stream);
 
 }  // namespace ua

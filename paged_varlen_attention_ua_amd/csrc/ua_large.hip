@@ -1,9 +1,11 @@
 // Large-query-block attention kernel for gfx950: prefill and chunked prefill.
 //
 // One workgroup owns (query block, kv head, key partition); a query block is
-// block_q = 128 / G tokens times the G query heads of the kv head (grouped
-// rows share every K/V tile).  Four waves own 32 rows each.  Per 64-key tile
-// (32 keys for head dim 256):
+// block_q = 32 NW / G tokens times the G query heads of the kv head (grouped
+// rows share every K/V tile).  NW = 4 or 8 waves own 32 rows each; every K/V
+// tile staged in LDS serves all of them, so 8 waves halve the K/V reads per
+// flop (they come from L2 and bound long chunks).  Per 64-key tile (32 keys for
+// head dim 256):
 //   * the byte offsets of the tile's K/V rows are looked up through the block
 //     table one tile ahead (its entries for the workgroup's key range are
 //     staged in LDS once) by one wave, into a small LDS table;
@@ -56,13 +58,20 @@ __device__ __forceinline__ u32x2 lds_read_tr16(const char* p) {
 }
 
 // Asynchronous 16-byte copy global -> LDS: lane i's 16 bytes land at
-// lds_uniform + 16 i (the LDS address is wave-uniform).  Completion is
-// tracked by vmcnt.
+// lds_uniform + 16 i (the LDS address is wave-uniform, passed in M0).
+// Completion is tracked by vmcnt.  Issued as inline assembly so that the
+// compiler does not track it: its wait insertion cannot tell the ring buffer
+// being copied into from the one being read and would drain every copy in
+// flight before each LDS read.  The kernel waits for each tile explicitly
+// (wait_vmem_n, then a barrier); vmcnt completes in issue order, so waits the
+// compiler computes for its own loads can only wait longer, never shorter.
+// M0 has no other use in this kernel.
 __device__ __forceinline__ void load_lds16(const char* src, char* lds_uniform) {
 #if defined(__HIP_DEVICE_COMPILE__)
-  __builtin_amdgcn_global_load_lds((const void*)src,
-                                   (__attribute__((address_space(3))) void*)lds_uniform, 16, 0,
-                                   0);
+  const uint32_t m0v = __builtin_amdgcn_readfirstlane(
+      (uint32_t)(uintptr_t)(__attribute__((address_space(3))) char*)lds_uniform);
+  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off" ::"s"(m0v), "v"(src)
+               : "memory");
 #else
   (void)src;
   (void)lds_uniform;
@@ -74,18 +83,41 @@ __device__ __forceinline__ void wait_vmem() {
   __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0), expcnt and lgkmcnt not waited on
 }
 
-template <int D>
+// Workgroup barrier that orders LDS only: this wave's LDS reads and writes
+// have completed (lgkmcnt(0)) before it arrives.  DMA copies into LDS are not
+// drained (__syncthreads() would wait for every outstanding global load,
+// including copies of tiles needed only several steps later); the ring waits
+// for exactly the tile it needs with wait_vmem_n before arriving.  The empty
+// asm statements keep the compiler from moving memory accesses across it.
+__device__ __forceinline__ void barrier_lds() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0); vmcnt and expcnt not waited on
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+// Wait until at most N of this wave's global loads are outstanding (gfx9
+// s_waitcnt: vmcnt bits 3:0 and 15:14; expcnt and lgkmcnt not waited on).
+template <int N>
+__device__ __forceinline__ void wait_vmem_n() {
+  static_assert(N >= 0 && N < 64, "vmcnt is six bits");
+  __builtin_amdgcn_s_waitcnt((N & 15) | (0x7 << 4) | (0xF << 8) | ((N >> 4) << 14));
+}
+
+template <int D, int NW>
 struct LargeCfg {
   static constexpr int TK = D > 128 ? 32 : 64;  // keys per tile
   static constexpr int NC = D / 8;               // 16-byte slots per K/V row (16-bit values)
   static constexpr int ROWB = 2 * D;             // LDS bytes per row
   static constexpr int TILEB = TK * ROWB;        // LDS bytes per K (or V) tile buffer
-  static constexpr int BPW = TILEB / 1024 / 4;   // 1 KiB copy blocks per wave per buffer
+  static constexpr int NT = 64 * NW;             // threads per workgroup
+  static constexpr int BPW = TILEB / 1024 / NW;  // 1 KiB copy blocks per wave per buffer
   static constexpr int KB = TK / 32;             // 32-key blocks per tile
   static constexpr int QC = D / 16;              // QK MFMAs per 32-key block
   static constexpr int DB = D / 32;              // PV output blocks of 32 head-dim rows
-  static constexpr int CPT = TK * NC / 256;      // slots per thread per tile (fp8 staging)
-  static constexpr int MAXPG = 1024;             // block-table entries staged in LDS
+  static constexpr int CPT = TK * NC / NT;       // slots per thread per tile (fp8 staging)
+  static constexpr int MAXPG = 2048;             // block-table entries staged in LDS
+  static_assert(BPW >= 1 && CPT >= 1, "tile too small for the workgroup");
 };
 
 // Physical 16-byte slot of logical slot c in LDS row r is c ^ swz<D>(r).
@@ -105,32 +137,49 @@ __device__ __forceinline__ int swz(int r) {
     return (((r >> 1) & 1) << 2) | ((r >> 2) & 3);
 }
 
-template <bool FP8, int D>
+template <bool FP8, int D, int NW>
 struct Stage {
   // fp8 staging only: 8 codes (2 dwords) per slot.
-  uint32_t k[FP8 ? LargeCfg<D>::CPT : 1][2];
-  uint32_t v[FP8 ? LargeCfg<D>::CPT : 1][2];
+  uint32_t k[FP8 ? LargeCfg<D, NW>::CPT : 1][2];
+  uint32_t v[FP8 ? LargeCfg<D, NW>::CPT : 1][2];
 };
 
 // Ring slots of the per-token scale buffer (one dummy slot without scales).
 template <bool ON>
 constexpr int tsc_lds() {
-  return ON ? 3 : 1;
+  return ON ? 3 : 1;  // per-token scales exist for fp8 only, whose ring is two deep
 }
 
-template <int QT, bool FP8, int D, bool SPLIT, bool FNUZ, bool TS>
-__global__ __launch_bounds__(256, (D > 128 ? 1 : 2)) void large_kernel(Params p) {
-  using C = LargeCfg<D>;
+// Workgroups per CU the register budget is sized for: two waves per SIMD
+// (four-wave groups, D <= 128; eight-wave groups), one for D = 256.
+template <int D, int NW>
+constexpr int large_min_groups() {
+  return NW == 8 ? 1 : (D > 128 ? 1 : 2);
+}
+
+template <int QT, bool FP8, int D, bool SPLIT, bool FNUZ, bool TS, int NW>
+__global__ __launch_bounds__(64 * NW, (large_min_groups<D, NW>())) void large_kernel(Params p) {
+  using C = LargeCfg<D, NW>;
   constexpr int TK = C::TK;
   constexpr int ROWB = C::ROWB;
+  // K/V tile ring: NBUF buffers each.  16-bit caches in eight-wave groups
+  // (one per CU, LDS to spare) run four deep, so a tile's copy is issued three
+  // tiles before it is used; otherwise two deep (measured on MI355X: four deep
+  // is 2-4% faster for eight-wave groups and 7% slower for D = 256).
+  constexpr int NBUF = (!FP8 && NW == 8) ? 4 : 2;
+  constexpr int TB2 = NBUF > 2 ? C::TILEB : 16;
   __shared__ __attribute__((aligned(1024))) char sK0[C::TILEB];
   __shared__ __attribute__((aligned(1024))) char sK1[C::TILEB];
+  __shared__ __attribute__((aligned(1024))) char sK2[TB2];
+  __shared__ __attribute__((aligned(1024))) char sK3[TB2];
   __shared__ __attribute__((aligned(1024))) char sV0[C::TILEB];
   __shared__ __attribute__((aligned(1024))) char sV1[C::TILEB];
-  __shared__ int64_t sTab0[TK];
-  __shared__ int64_t sTab1[TK];
+  __shared__ __attribute__((aligned(1024))) char sV2[TB2];
+  __shared__ __attribute__((aligned(1024))) char sV3[TB2];
+  // Row-offset table of tile t in slot t % NBUF.
+  __shared__ int64_t sTab[NBUF][TK];
   __shared__ int32_t sm_pg[C::MAXPG];
-  // Per-token scales of tile t in ring slot t % 3: [slot][0: K, 1: V][key].
+  // Per-token scales of tile t in ring slot t % (NBUF + 1): [slot][0: K, 1: V][key].
   __shared__ __attribute__((aligned(16))) float sSc[tsc_lds<FP8 && TS>()][2][TK];
 
   const int tid = threadIdx.x;
@@ -235,8 +284,12 @@ __global__ __launch_bounds__(256, (D > 128 ? 1 : 2)) void large_kernel(Params p)
   const int pg_first = (int)fastdiv((uint32_t)kl, p.bs_div);
   {
     const int npg = min((int)fastdiv((uint32_t)(k1 - 1), p.bs_div) - pg_first + 1, C::MAXPG);
-    for (int j = tid; j < npg; j += 256) sm_pg[j] = bt_row[pg_first + j];
+    for (int j = tid; j < npg; j += C::NT) sm_pg[j] = bt_row[pg_first + j];
   }
+  // Every load issued so far (Q operands, slopes, block-table entries) has
+  // landed: from here on outstanding vector loads are the tile copies, and no
+  // compiler-placed wait for these registers can fall inside the copy ring.
+  wait_vmem();
   __syncthreads();
 
   // Row byte offsets (page * block stride + slot * slot stride) of keys
@@ -253,7 +306,15 @@ __global__ __launch_bounds__(256, (D > 128 ? 1 : 2)) void large_kernel(Params p)
       const uint32_t bi = fastdiv((uint32_t)key, p.bs_div);
       const int slot = key - (int)bi * p.block_size;
       const int j = (int)bi - pg_first;
-      const int32_t page = j < C::MAXPG ? sm_pg[j] : bt_row[bi];
+      int32_t page;
+      if (j < C::MAXPG) {
+        page = sm_pg[j];
+      } else {
+        // Rare (ranges beyond the staged entries): settle this load here so
+        // that the common path waits on LDS only, not on the copies in flight.
+        page = bt_row[bi];
+        wait_vmem();
+      }
       tab[lane] = (int64_t)page * blk_b + (int64_t)slot * slot_b;
       if constexpr (tsc) {
         sc_k = p.k_tscale[(int64_t)kvh * p.ks_stride_head +
@@ -266,23 +327,24 @@ __global__ __launch_bounds__(256, (D > 128 ? 1 : 2)) void large_kernel(Params p)
   auto store_sc = [&](int tile) __attribute__((always_inline)) {
     if constexpr (tsc) {
       if (lane < TK) {
-        float* dst = &sSc[tile % 3][0][0];
+        float* dst = &sSc[tile % tsc_lds<tsc>()][0][0];
         dst[lane] = sc_k;
         dst[TK + lane] = sc_v;
       }
     }
   };
 
-  // 16-bit caches: copy block b = 4u + wave (1 KiB = 64 slots) of a tile;
+  // 16-bit caches: copy block b = NW u + wave (1 KiB = 64 slots) of a tile;
   // lane i fills physical slot n = 64 b + i, i.e. row n / NC, logical slot
   // (n % NC) ^ swz(row).  swz reads bits 0..3 of the row, which depend on u
-  // only for 32-slot rows (through u % 2): NSRC distinct per-lane sources.
-  constexpr int NSRC = (C::NC == 32 && C::BPW > 1) ? 2 : 1;
+  // only for 32-slot rows with four waves (through u % 2): NSRC distinct
+  // per-lane sources.
+  constexpr int NSRC = (C::NC == 32 && NW == 4 && C::BPW > 1) ? 2 : 1;
   const char* ksrc[NSRC];
   const char* vsrc[NSRC];
 #pragma unroll
   for (int u = 0; u < NSRC; ++u) {
-    const int n = 64 * (4 * u + wave) + lane;
+    const int n = 64 * (NW * u + wave) + lane;
     const int r = n / C::NC;
     const int c = (n % C::NC) ^ swz<D>(r);
     ksrc[u] = kbase + 16 * c;
@@ -291,20 +353,20 @@ __global__ __launch_bounds__(256, (D > 128 ? 1 : 2)) void large_kernel(Params p)
   auto issue_copy = [&](char* dk, char* dv, const int64_t* tab) __attribute__((always_inline)) {
 #pragma unroll
     for (int u = 0; u < C::BPW; ++u) {
-      const int b = 4 * u + wave;
+      const int b = NW * u + wave;
       const int64_t off = tab[(64 * b + lane) / C::NC];
       load_lds16(ksrc[u % NSRC] + off, dk + 1024 * b);
       load_lds16(vsrc[u % NSRC] + off, dv + 1024 * b);
     }
   };
 
-  // fp8 caches: thread slot i = tid + 256 u is row i / NC, logical slot i % NC.
-  Stage<FP8, D> st;
+  // fp8 caches: thread slot i = tid + NT u is row i / NC, logical slot i % NC.
+  Stage<FP8, D, NW> st;
   auto stage_load = [&](const int64_t* tab) __attribute__((always_inline)) {
     if constexpr (FP8) {
 #pragma unroll
       for (int u = 0; u < C::CPT; ++u) {
-        const int i = tid + 256 * u;
+        const int i = tid + C::NT * u;
         const int64_t off = tab[i / C::NC] + 8 * (i % C::NC);
         const u32x2 a = *reinterpret_cast<const u32x2*>(kbase + off);
         const u32x2 b = *reinterpret_cast<const u32x2*>(vbase + off);
@@ -317,7 +379,7 @@ __global__ __launch_bounds__(256, (D > 128 ? 1 : 2)) void large_kernel(Params p)
     if constexpr (FP8) {
 #pragma unroll
       for (int u = 0; u < C::CPT; ++u) {
-        const int i = tid + 256 * u;
+        const int i = tid + C::NT * u;
         const int r = i / C::NC;
         const int at = r * ROWB + 16 * ((i % C::NC) ^ swz<D>(r));
         *reinterpret_cast<u32x4*>(dk + at) = fp8x8_to<QT, FNUZ>(u32x2{st.k[u][0], st.k[u][1]});
@@ -493,59 +555,89 @@ __global__ __launch_bounds__(256, (D > 128 ? 1 : 2)) void large_kernel(Params p)
     }
   };
 
-  // Prologue: tables (and scales) of tiles 0 and 1, then tile 0 into buffer 0.
-  if (wave == 0) {
-    fill_tab(sTab0, k0);
-    store_sc(0);
-  }
-  if (wave == 1 && ntiles > 1) {
-    fill_tab(sTab1, k0 + TK);
-    store_sc(1);
+  // Buffer B of the ring (compile-time B).
+  auto kbuf = [&](auto bc) __attribute__((always_inline)) -> char* {
+    constexpr int B = decltype(bc)::value % NBUF;
+    if constexpr (B == 0) return sK0;
+    else if constexpr (B == 1) return sK1;
+    else if constexpr (B == 2) return sK2;
+    else return sK3;
+  };
+  auto vbuf = [&](auto bc) __attribute__((always_inline)) -> char* {
+    constexpr int B = decltype(bc)::value % NBUF;
+    if constexpr (B == 0) return sV0;
+    else if constexpr (B == 1) return sV1;
+    else if constexpr (B == 2) return sV2;
+    else return sV3;
+  };
+  using I0 = std::integral_constant<int, 0>;
+  using I1 = std::integral_constant<int, 1>;
+  using I2 = std::integral_constant<int, 2>;
+  using I3 = std::integral_constant<int, 3>;
+  // Copy instructions one wave issues per tile (K and V).
+  constexpr int CPW = 2 * C::BPW;
+
+  // Prologue: tables (and scales) of tiles 0 .. NBUF - 1, one wave each; then
+  // tiles 0 .. NBUF - 2 are copied (fp8: tile 0 staged) and tile 0 waited for.
+  if (wave < NBUF && wave < ntiles) {
+    fill_tab(sTab[wave], k0 + wave * TK);
+    store_sc(wave);
   }
   __syncthreads();
   if constexpr (FP8) {
-    stage_load(sTab0);
+    stage_load(sTab[0]);
     stage_store(sK0, sV0);
   } else {
-    issue_copy(sK0, sV0, sTab0);
-    wait_vmem();
+    issue_copy(sK0, sV0, sTab[0]);
+    if constexpr (NBUF > 2) {
+      if (ntiles > 1) issue_copy(kbuf(I1{}), vbuf(I1{}), sTab[1]);
+      if (ntiles > 2) issue_copy(kbuf(I2{}), vbuf(I2{}), sTab[2]);
+      if (ntiles > 2)
+        wait_vmem_n<2 * CPW>();
+      else
+        wait_vmem();
+    } else {
+      wait_vmem();
+    }
   }
-  __syncthreads();
+  barrier_lds();
 
-  // Tile t lives in buffer t % 2 and its row table in table t % 2.  While it
-  // is computed, tile t + 1 is copied into the other buffer and one wave
-  // fills the table of tile t + 2 (the table tile t was copied with).
+  // Step t (tile t in buffer t % NBUF): issue the copy of tile t + NBUF - 1
+  // (fp8: stage tile t + 1 in registers), let one wave fill the table of tile
+  // t + NBUF (the slot tile t was copied with), compute tile t, then wait until
+  // tile t + 1 has landed while later tiles' copies stay in flight.
   auto step = [&](auto bufc, int t) __attribute__((always_inline)) {
     constexpr int B = decltype(bufc)::value;
-    char* cur_k = B ? sK1 : sK0;
-    char* cur_v = B ? sV1 : sV0;
-    char* nxt_k = B ? sK0 : sK1;
-    char* nxt_v = B ? sV0 : sV1;
-    const int64_t* tab_next = B ? sTab0 : sTab1;
-    int64_t* tab_fill = B ? sTab1 : sTab0;
+    using NB = std::integral_constant<int, (B + NBUF - 1) % NBUF>;
     const int kt = k0 + t * TK;
-    const bool more = t + 1 < ntiles;
-    if (more) {
-      if constexpr (FP8)
-        stage_load(tab_next);
-      else
-        issue_copy(nxt_k, nxt_v, tab_next);
+    const bool copy = t + NBUF - 1 < ntiles;
+    if constexpr (FP8) {
+      if (copy) stage_load(sTab[NB::value]);
+    } else {
+      if (copy) issue_copy(kbuf(NB{}), vbuf(NB{}), sTab[NB::value]);
     }
-    const bool filler = t + 2 < ntiles && wave == (t & 3);
-    if (filler) fill_tab(tab_fill, kt + 2 * TK);
-    if (wave_live) compute(cur_k, cur_v, kt, &sSc[tsc ? t % 3 : 0][0][0]);
-    if (more) {
-      if constexpr (FP8)
-        stage_store(nxt_k, nxt_v);
+    const bool filler = t + NBUF < ntiles && wave == (t & (NW - 1));
+    if (filler) fill_tab(sTab[B], kt + NBUF * TK);
+    if (wave_live) compute(kbuf(bufc), vbuf(bufc), kt, &sSc[tsc ? t % tsc_lds<tsc>() : 0][0][0]);
+    if constexpr (FP8) {
+      if (copy) stage_store(kbuf(NB{}), vbuf(NB{}));
+    } else if (t + 1 < ntiles) {
+      if (copy)
+        wait_vmem_n<(NBUF - 2) * CPW>();
       else
         wait_vmem();
     }
-    if (filler) store_sc(t + 2);
-    __syncthreads();
+    if (filler) store_sc(t + NBUF);
+    barrier_lds();
   };
-  for (int t = 0; t < ntiles; t += 2) {
-    step(std::integral_constant<int, 0>{}, t);
-    if (t + 1 < ntiles) step(std::integral_constant<int, 1>{}, t + 1);
+  static_assert(NBUF == 2 || NBUF == 4, "ring depth");
+  for (int t = 0; t < ntiles; t += NBUF) {
+    step(I0{}, t);
+    if (t + 1 < ntiles) step(I1{}, t + 1);
+    if constexpr (NBUF > 2) {
+      if (t + 2 < ntiles) step(I2{}, t + 2);
+      if (t + 3 < ntiles) step(I3{}, t + 3);
+    }
   }
 
   if (!row_ok) return;
@@ -590,48 +682,72 @@ __global__ __launch_bounds__(256, (D > 128 ? 1 : 2)) void large_kernel(Params p)
 }
 
 template <int QT, bool FP8, int D, bool FNUZ, bool TS>
-hipError_t launch_large_t(const Params& p, bool split, dim3 grid, hipStream_t stream) {
+hipError_t launch_large_t(const Params& p, bool split, bool eight, dim3 grid, hipStream_t stream) {
+  if constexpr (D <= 128) {
+    if (eight) {
+      if (split)
+        hipLaunchKernelGGL((large_kernel<QT, FP8, D, true, FNUZ, TS, 8>), grid, dim3(512), 0,
+                           stream, p);
+      else
+        hipLaunchKernelGGL((large_kernel<QT, FP8, D, false, FNUZ, TS, 8>), grid, dim3(512), 0,
+                           stream, p);
+      return hipGetLastError();
+    }
+  } else {
+    if (eight) return hipErrorInvalidValue;
+  }
   if (split)
-    hipLaunchKernelGGL((large_kernel<QT, FP8, D, true, FNUZ, TS>), grid, dim3(256), 0, stream, p);
+    hipLaunchKernelGGL((large_kernel<QT, FP8, D, true, FNUZ, TS, 4>), grid, dim3(256), 0, stream,
+                       p);
   else
-    hipLaunchKernelGGL((large_kernel<QT, FP8, D, false, FNUZ, TS>), grid, dim3(256), 0, stream, p);
+    hipLaunchKernelGGL((large_kernel<QT, FP8, D, false, FNUZ, TS, 4>), grid, dim3(256), 0, stream,
+                       p);
   return hipGetLastError();
 }
 
 template <int QT, bool FP8, bool FNUZ, bool TS>
-hipError_t launch_large_d(const Params& p, int head_dim, bool split, dim3 grid,
+hipError_t launch_large_d(const Params& p, int head_dim, bool split, bool eight, dim3 grid,
                           hipStream_t stream) {
   switch (head_dim) {
-    case 64: return launch_large_t<QT, FP8, 64, FNUZ, TS>(p, split, grid, stream);
-    case 128: return launch_large_t<QT, FP8, 128, FNUZ, TS>(p, split, grid, stream);
-    case 256: return launch_large_t<QT, FP8, 256, FNUZ, TS>(p, split, grid, stream);
+    case 64: return launch_large_t<QT, FP8, 64, FNUZ, TS>(p, split, eight, grid, stream);
+    case 128: return launch_large_t<QT, FP8, 128, FNUZ, TS>(p, split, eight, grid, stream);
+    case 256: return launch_large_t<QT, FP8, 256, FNUZ, TS>(p, split, eight, grid, stream);
     default: return hipErrorInvalidValue;
   }
 }
 
 // Per-token scales are a template switch: kernels without them are unchanged.
 template <int QT>
-hipError_t launch_large_q(const Params& p, int kv_fmt, int head_dim, bool split, dim3 grid,
-                          hipStream_t stream) {
+hipError_t launch_large_q(const Params& p, int kv_fmt, int head_dim, bool split, bool eight,
+                          dim3 grid, hipStream_t stream) {
   const bool ts = p.k_tscale != nullptr;
   switch (kv_fmt) {
-    case kKv16: return launch_large_d<QT, false, false, false>(p, head_dim, split, grid, stream);
+    case kKv16:
+      return launch_large_d<QT, false, false, false>(p, head_dim, split, eight, grid, stream);
     case kKvE4m3fn:
-      return ts ? launch_large_d<QT, true, false, true>(p, head_dim, split, grid, stream)
-                : launch_large_d<QT, true, false, false>(p, head_dim, split, grid, stream);
+      return ts ? launch_large_d<QT, true, false, true>(p, head_dim, split, eight, grid, stream)
+                : launch_large_d<QT, true, false, false>(p, head_dim, split, eight, grid, stream);
     case kKvE4m3fnuz:
-      return ts ? launch_large_d<QT, true, true, true>(p, head_dim, split, grid, stream)
-                : launch_large_d<QT, true, true, false>(p, head_dim, split, grid, stream);
+      return ts ? launch_large_d<QT, true, true, true>(p, head_dim, split, eight, grid, stream)
+                : launch_large_d<QT, true, true, false>(p, head_dim, split, eight, grid, stream);
     default: return hipErrorInvalidValue;
   }
 }
 
 }  // namespace
 
-hipError_t launch_large(const Params& p, int q_dtype, int kv_fmt, int head_dim, bool split,
-                        dim3 grid, hipStream_t stream) {
-  return q_dtype == UA_F16 ? launch_large_q<UA_F16>(p, kv_fmt, head_dim, split, grid, stream)
-                           : launch_large_q<UA_BF16>(p, kv_fmt, head_dim, split, grid, stream);
+// One entry per query dtype (see launch_small_f16 for the UA_QT split).
+#if !defined(UA_QT) || UA_QT == 0
+hipError_t launch_large_f16(const Params& p, int kv_fmt, int head_dim, bool split,
+                            bool eight_waves, dim3 grid, hipStream_t stream) {
+  return launch_large_q<UA_F16>(p, kv_fmt, head_dim, split, eight_waves, grid, stream);
 }
+#endif
+#if !defined(UA_QT) || UA_QT == 1
+hipError_t launch_large_bf16(const Params& p, int kv_fmt, int head_dim, bool split,
+                             bool eight_waves, dim3 grid, hipStream_t stream) {
+  return launch_large_q<UA_BF16>(p, kv_fmt, head_dim, split, eight_waves, grid, stream);
+}
+#endif
 
 }  // namespace ua

@@ -740,10 +740,20 @@ hipError_t launch_small_q(const Params& p, int kv_fmt, int head_dim, bool split,
 
 }  // namespace
 
-hipError_t launch_small(const Params& p, int q_dtype, int kv_fmt, int head_dim, bool split,
-                        dim3 grid, hipStream_t stream) {
-  return q_dtype == UA_F16 ? launch_small_q<UA_F16>(p, kv_fmt, head_dim, split, grid, stream)
-                           : launch_small_q<UA_BF16>(p, kv_fmt, head_dim, split, grid, stream);
+// One entry per query dtype; the build compiles this file once per dtype
+// (UA_QT = 0: fp16, 1: bf16) so the two halves of the instantiations compile in
+// parallel.  Without UA_QT both are defined.
+#if !defined(UA_QT) || UA_QT == 0
+hipError_t launch_small_f16(const Params& p, int kv_fmt, int head_dim, bool split, dim3 grid,
+                            hipStream_t stream) {
+  return launch_small_q<UA_F16>(p, kv_fmt, head_dim, split, grid, stream);
 }
+#endif
+#if !defined(UA_QT) || UA_QT == 1
+hipError_t launch_small_bf16(const Params& p, int kv_fmt, int head_dim, bool split, dim3 grid,
+                             hipStream_t stream) {
+  return launch_small_q<UA_BF16>(p, kv_fmt, head_dim, split, grid, stream);
+}
+#endif
 
 }  // namespace ua

@@ -171,7 +171,7 @@ def test_per_token_scales(kvd, shape, bs):
     assert case["k_token_scales"].strides != case["v_token_scales"].strides
     for path, n_part in [("2d", 0), ("splitkv", 3), ("auto", 0)]:
         _, plan = _check(case, path, n_part, label=f"{kvd}-{shape}-bs{bs}-{path}{n_part}")
-        assert plan.kernel == (0 if shape == "decode" else 1)
+        assert (plan.kernel == 0) == (shape == "decode")
 
 
 @pytest.mark.parametrize("D", [64, 256])
@@ -205,6 +205,22 @@ def test_per_token_tile_ring_lengths():
         for n_part in (1, 2, 3):
             path = "2d" if n_part == 1 else "splitkv"
             _check(case, path, n_part, label=f"kv{kv}-w{w}-p{n_part}")
+
+
+def test_deep_copy_ring_tile_counts():
+    """16-bit K/V copy ring (two deep for D = 256, four deep for 256-row
+    blocks): key ranges and partitions of 1 .. 7 tiles (copies still in flight
+    when a partition ends)."""
+    for kv in (20, 40, 70, 100, 130, 200):  # D = 256: 32-key tiles
+        case = make_case(seqs=[(17, kv), (5, kv + 9)], seed=100 + kv,
+                         **dict(BASE, head_dim=256))
+        _, plan = _check(case, "2d", 0, label=f"d256-kv{kv}")
+        assert plan.kernel == 1
+    case = make_case(seqs=[(300, 4400), (40, 4200)], seed=120, **BASE)
+    for n_part in (1, 17, 33, 70):  # 256-row blocks, 64-key tiles
+        path = "2d" if n_part == 1 else "splitkv"
+        _, plan = _check(case, path, n_part, label=f"rows256-p{n_part}")
+        assert plan.kernel == 2
 
 
 @pytest.mark.parametrize("Hq,Hkv", [(4, 4), (6, 2), (24, 4), (32, 2), (8, 1)])
