@@ -178,6 +178,8 @@ Params make_params(const ua_problem* p, const ua_plan_t* plan, const ua_args* a,
   q.num_q_heads = p->num_q_heads;
   q.num_kv_heads = p->num_kv_heads;
   q.group = p->num_q_heads / p->num_kv_heads;
+  q.head_groups = plan->grid_y / p->num_kv_heads;
+  q.group_rows = q.group / q.head_groups;
   q.block_size = p->block_size;
   q.max_blocks_per_seq = p->max_blocks_per_seq;
   q.bs_div = make_fastdiv((uint32_t)p->block_size);
@@ -241,20 +243,34 @@ ua_status ua_plan(const ua_problem* prob, int32_t num_cus, int32_t force_path,
   // (measured on MI355X: a few % faster there; slower on shorter ranges and
   // for fp8 caches, where two independent four-wave groups per CU overlap
   // better), else 128 rows.
-  const bool small = G <= kSmallRows && (int64_t)prob->max_seqlen_q * G <= kSmallRows;
+  // Decode (one query per sequence) with G > 16: split each kv head's query
+  // heads into HG groups of at most 16, one small block each (they read the
+  // same K/V rows), instead of a large block with most MFMA rows idle.
+  int HG = 1;
+  if (G > kSmallRows && prob->max_seqlen_q <= 1) {
+    for (int h = 2; h <= G; ++h) {
+      if (G % h == 0 && G / h <= kSmallRows) {
+        HG = h;
+        break;
+      }
+    }
+  }
+  const int Gs = G / HG;  // query heads per block and token
+  const bool small = Gs <= kSmallRows && (int64_t)prob->max_seqlen_q * Gs <= kSmallRows;
+  if (!small) HG = 1;
   int64_t eff_k = prob->max_seqlen_k;
   if (prob->window > 0)
     eff_k = std::min<int64_t>(eff_k, (int64_t)prob->window + prob->max_seqlen_q - 1);
   const bool eight = !small && prob->head_dim <= 128 && is_16bit(prob->kv_dtype) &&
                      (int64_t)prob->max_seqlen_q * G >= kLarge8Rows && eff_k >= 4096;
   plan->kernel = small ? 0 : (eight ? 2 : 1);
-  plan->block_q = small ? kSmallRows / G : (eight ? kLarge8Rows : kLargeRows) / G;
+  plan->block_q = small ? kSmallRows / Gs : (eight ? kLarge8Rows : kLargeRows) / G;
   const int bq = plan->block_q;
   const int64_t slots = prob->num_seqs > 0 ? (int64_t)prob->total_q / bq + prob->num_seqs : 0;
   const int64_t est_blocks =
       std::min<int64_t>(slots, (int64_t)prob->num_seqs * ceil_div(prob->max_seqlen_q, bq));
   if (prob->window > 0) eff_k = std::min<int64_t>(eff_k, (int64_t)prob->window + bq - 1);
-  const int64_t wgs = est_blocks * prob->num_kv_heads;
+  const int64_t wgs = est_blocks * prob->num_kv_heads * HG;
 
   // Automatic partition count: fill about four small workgroups per CU,
   // keep at least 256 keys per partition, and stay one-pass for short ranges.
@@ -297,7 +313,7 @@ ua_status ua_plan(const ua_problem* prob, int32_t num_cus, int32_t force_path,
     plan->flags |= 1;
     plan->grid_x = prob->num_seqs;
   }
-  plan->grid_y = prob->num_kv_heads;
+  plan->grid_y = prob->num_kv_heads * HG;
   plan->grid_z = n_part;
   plan->workspace_bytes =
       plan->path == UA_PATH_SPLITKV
@@ -319,6 +335,10 @@ static ua_status check_plan(const ua_problem* prob, const ua_plan_t* plan, int32
   if (st != UA_OK) return st;
   if (plan->problem_hash != problem_hash(prob) || plan->path != path) return UA_EPLAN;
   if (plan->n_part < 1 || plan->block_q < 1 || plan->kernel < 0 || plan->kernel > 2)
+    return UA_EPLAN;
+  if (plan->grid_y < prob->num_kv_heads || plan->grid_y % prob->num_kv_heads != 0 ||
+      (prob->num_q_heads / prob->num_kv_heads) % (plan->grid_y / prob->num_kv_heads) != 0 ||
+      (plan->kernel != 0 && plan->grid_y != prob->num_kv_heads))
     return UA_EPLAN;
   return UA_OK;
 }

@@ -82,6 +82,8 @@ struct Params {
   int32_t grid_x;       // number of query-block slots launched along x
   int32_t seq_blocks;   // 1: block x is the sequence index (every query run fits one block)
   int32_t qq_stride;    // QQ-bias row stride (elements)
+  int32_t head_groups;  // blocks per kv head along y (small kernel; 1 otherwise)
+  int32_t group_rows;   // query heads per block and token: group / head_groups
 };
 
 // Storage format of the K/V cache as the kernels see it.

@@ -4,6 +4,8 @@
 // block_q consecutive query tokens of one sequence times the G = Hq / Hkv query
 // heads that share the kv head (grouped-query packing: every row of the block
 // reads the same K/V rows), at most 16 rows: the N side of a 16x16x32 MFMA.
+// Decode with G > 16 (e.g. multi-query attention) splits the G heads into
+// groups of at most 16, one block each, which read the same K/V rows.
 // The four waves of the workgroup walk interleaved 32-key tiles of the
 // partition, each keeping its own online-softmax state (running max m, sum l
 // and output accumulator, AITER PR #3962 review diff), and merge through LDS at
@@ -262,7 +264,12 @@ __global__ __launch_bounds__(64 * kSmallWaves, 2) void small_kernel(Params p) {
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int g = lane >> 4, r16 = lane & 15;
-  const int qb = blockIdx.x, kvh = blockIdx.y, part = blockIdx.z;
+  const int qb = blockIdx.x, part = blockIdx.z;
+  // blockIdx.y = kv head x head groups + group: decode with G > 16 splits a kv
+  // head's query heads into head_groups groups of group_rows heads, one block each.
+  const int HG = p.head_groups;
+  const int kvh = HG == 1 ? (int)blockIdx.y : (int)blockIdx.y / HG;
+  const int hg = (int)blockIdx.y - kvh * HG;
 
   int s, tok0;
   if (p.seq_blocks) {
@@ -286,7 +293,8 @@ __global__ __launch_bounds__(64 * kSmallWaves, 2) void small_kernel(Params p) {
   const int k0 = lo_a + part * plen;
   const int k1 = min(k0 + plen, hi);
   const int kl = max(k0, lo);
-  const int G = p.group;
+  const int G = p.group_rows;                    // query heads of this block per token
+  const int hbase = kvh * p.group + hg * G;      // head of block row 0
   const int R = p.total_q * p.num_q_heads;
 
   __shared__ float sm_m[kSmallWaves][16];
@@ -299,7 +307,7 @@ __global__ __launch_bounds__(64 * kSmallWaves, 2) void small_kernel(Params p) {
       if (tid < 16) {
         const int rt = tid / G, rh = tid - (tid / G) * G;
         if (tid < p.block_q * G && rt < ntok) {
-          const int64_t row = (int64_t)(tok0 + rt) * p.num_q_heads + kvh * G + rh;
+          const int64_t row = (int64_t)(tok0 + rt) * p.num_q_heads + hbase + rh;
           p.ws_l[(int64_t)part * R + row] = 0.0f;
           p.ws_m[(int64_t)part * R + row] = -INFINITY;
         }
@@ -332,7 +340,7 @@ __global__ __launch_bounds__(64 * kSmallWaves, 2) void small_kernel(Params p) {
   // This lane's query row.
   const int rt = r16 / G, rh = r16 - rt * G;
   const bool row_ok = (r16 < p.block_q * G) && (rt < ntok);
-  const int h = kvh * G + rh;
+  const int h = hbase + rh;
   const int pos = p0 + rt;
   const int row_lo = p.window > 0 ? max(kl, pos - p.window + 1) : kl;
   const int row_hi = min(k1, pos + 1);
@@ -632,7 +640,7 @@ __global__ __launch_bounds__(64 * kSmallWaves, 2) void small_kernel(Params p) {
     const int row = idx >> 4, chunk = idx & 15;
     const int mrt = row / G, mrh = row - (row / G) * G;
     if (!(row < p.block_q * G && mrt < ntok)) continue;
-    const int tok = tok0 + mrt, hh = kvh * G + mrh;
+    const int tok = tok0 + mrt, hh = hbase + mrh;
     float mw[kSmallWaves];
     float M = -INFINITY;
 #pragma unroll

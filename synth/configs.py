@@ -35,6 +35,7 @@ C5B = dict(C5A, seqs=[(2048, 18432)], seed=115)
 C5C = dict(C5A, seqs=[(1024, 1024)] * 4, seed=125)
 C5D = dict(seqs=[(8192, 8192)], head_dim=256, num_q_heads=24, num_kv_heads=4,
            block_size=784, q_dtype="bf16", seed=135)
+C5E = dict(C5A, seqs=[(8192, 8192)], seed=145)  # optional (e): the 8k prompt at D = 128
 
 # QQ-bias scenario of the RocKE README ("qq_bias_prefill_d128_b16": the
 # prefill_d128_b16 sequences with a QQ-bias of row stride 256).
@@ -84,6 +85,7 @@ WORKLOADS = {
     "prefill_chunk2k_prefix16k_bf16": C5B,
     "prefill_4x1k_bf16": C5C,
     "prefill_8k_d256_24q4kv_bs784_bf16": C5D,
+    "prefill_8k_d128_bf16": C5E,
     "qq_bias_prefill_fp16_d128_16q2kv": QQ,
     "d64_chunked_prefill_bf16_64q8kv_bs32_sinks_w128": D64_SW,
     "d64_prefill_bf16q_fp8kv_64q8kv_bs32_sinks": D64_FP8,
@@ -124,4 +126,5 @@ PREFILL_WORKLOADS = [
     "prefill_chunk2k_prefix16k_bf16",
     "prefill_4x1k_bf16",
     "prefill_8k_d256_24q4kv_bs784_bf16",
+    "prefill_8k_d128_bf16",
 ]

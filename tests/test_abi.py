@@ -88,6 +88,21 @@ def test_short_context_full_grid_stays_one_pass():
     assert plan.workspace_bytes == 0
 
 
+def test_wide_group_decode_splits_heads_into_small_blocks():
+    # MQA-style decode, 32 query heads on one kv head: two groups of 16 rows
+    st, plan = status_of(problem(num_q_heads=32, num_kv_heads=1, kv_stride_block=16 * 128,
+                                 kv_stride_slot=128))
+    assert st == 0 and plan.kernel == 0 and plan.grid_y == 2 and plan.block_q == 1
+    # 24 heads: two groups of 12
+    st, plan = status_of(problem(num_q_heads=24, num_kv_heads=1, kv_stride_block=16 * 128,
+                                 kv_stride_slot=128))
+    assert st == 0 and plan.kernel == 0 and plan.grid_y == 2 and plan.block_q == 1
+    # more than one query per sequence: large kernel, one block per kv head
+    st, plan = status_of(problem(num_q_heads=32, num_kv_heads=1, kv_stride_block=16 * 128,
+                                 kv_stride_slot=128, max_seqlen_q=2, total_q=16))
+    assert st == 0 and plan.kernel == 1 and plan.grid_y == 1
+
+
 def test_forced_paths():
     st, plan = status_of(problem(), force_path=B.UA_PATH_2D)
     assert st == 0 and plan.path == B.UA_PATH_2D and plan.n_part == 1

@@ -57,7 +57,7 @@ def test_workload_full_size(name, path, n_part):
 
 
 PREFILL = ["prefill_chunk1k_prefix8k_bf16", "prefill_chunk2k_prefix16k_bf16",
-           "prefill_4x1k_bf16", "prefill_8k_d256_24q4kv_bs784_bf16"]
+           "prefill_4x1k_bf16", "prefill_8k_d256_24q4kv_bs784_bf16", "prefill_8k_d128_bf16"]
 
 
 @pytest.mark.parametrize("path,n_part", [("auto", 0), ("splitkv", 3)])
@@ -73,6 +73,36 @@ def test_prefill_full_size_sampled_rows(name, path, n_part):
     err = compare(case, got, ref, rows=rows, label=name)
     check_lse(lse[rows], ref_lse, label=name)
     print(f"[ok] {name} path={plan.path} max_abs={err:.3e}", flush=True)
+
+
+@pytest.mark.parametrize("extra", [1000, 2000, 3000])
+@pytest.mark.parametrize("name", DECODE_AND_MIXED)
+def test_workload_extra_seeds(name, extra):
+    """Each decode / mixed workload on three more seeds (auto path)."""
+    kw = dict(WORKLOADS[name])
+    kw["seed"] = kw["seed"] + extra
+    case = make_case(**kw)
+    print(f"[case] {name} seed={kw['seed']}", flush=True)
+    ref, ref_lse = oracle.attention(**case)
+    got, lse, plan = run(case, lse=True)
+    err = compare(case, got, ref, label=f"{name}/seed{kw['seed']}")
+    check_lse(lse, ref_lse, label=name)
+    print(f"[ok] {name} seed={kw['seed']} max_abs={err:.3e}", flush=True)
+
+
+@pytest.mark.parametrize("extra", [1000, 2000, 3000])
+@pytest.mark.parametrize("name", PREFILL)
+def test_prefill_extra_seeds_sampled_rows(name, extra):
+    kw = dict(WORKLOADS[name])
+    kw["seed"] = kw["seed"] + extra
+    case = make_case(**kw)
+    rows = sample_rows(case["q"].shape[0], 24, seed=extra)
+    ref, ref_lse = oracle.attention(**case, rows=rows)
+    print(f"[case] {name} seed={kw['seed']} rows={len(rows)}", flush=True)
+    got, lse, plan = run(case, lse=True)
+    assert np.isfinite(got).all(), "unwritten or NaN output rows"
+    compare(case, got, ref, rows=rows, label=f"{name}/seed{kw['seed']}")
+    check_lse(lse[rows], ref_lse, label=name)
 
 
 NEXT_DECODE = NEXT_DECODE_WORKLOADS
@@ -221,6 +251,18 @@ def test_deep_copy_ring_tile_counts():
         path = "2d" if n_part == 1 else "splitkv"
         _, plan = _check(case, path, n_part, label=f"rows256-p{n_part}")
         assert plan.kernel == 2
+
+
+@pytest.mark.parametrize("Hq,Hkv", [(24, 1), (32, 1), (64, 2)])
+def test_wide_group_decode_head_groups(Hq, Hkv):
+    """Decode with G > 16 runs as head groups of <= 16 rows on the small kernel;
+    per-head sinks and ALiBi slopes catch a wrong head mapping."""
+    seqs = [(1, 300), (1, 90), (0, 12), (1, 1), (1, 700), (1, 1500)]
+    case = make_case(seqs=seqs, seed=130 + Hq, sinks=True, alibi=True, window=600,
+                     **dict(BASE, num_q_heads=Hq, num_kv_heads=Hkv))
+    for path, n_part in [("2d", 0), ("splitkv", 3), ("auto", 0)]:
+        _, plan = _check(case, path, n_part, label=f"G{Hq // Hkv}-{path}{n_part}")
+        assert plan.kernel == 0 and plan.grid_y > Hkv
 
 
 @pytest.mark.parametrize("Hq,Hkv", [(4, 4), (6, 2), (24, 4), (32, 2), (8, 1)])
