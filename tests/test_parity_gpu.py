@@ -343,6 +343,50 @@ def test_repeat_is_bit_identical():
     assert np.array_equal(c, d)
 
 
+@pytest.mark.parametrize("path,n_part", [("2d", 0), ("splitkv", 4)])
+def test_graph_capture_replays(path, n_part):
+    """One forward (split: partition kernel + reduce) captured in a HIP graph and
+    replayed several times, with eager work and an input change in between:
+    every replay equals an eager run on the same inputs, bit for bit."""
+    import paged_varlen_attention_ua_amd.attention as A
+    case, ref, _ = _workload("long_decode_bf16_d128_32q8kv_w4096_softcap_sinks")
+    d = {k: (v.clone() if v is not None else None)
+         for k, v in _dev("long_decode_bf16_d128_32q8kv_w4096_softcap_sinks").items()}
+    kw = dict(max_seqlen_q=case["max_seqlen_q"], max_seqlen_k=case["max_seqlen_k"],
+              scale=case["scale"], softcap=case["softcap"], window=case["window"],
+              sinks=d["sinks"], path=path, n_part=n_part)
+    args = (d["q"], d["k_cache"], d["v_cache"], d["block_table"], d["cu_seqlens_q"],
+            d["seq_lens"])
+    out = torch.full_like(d["q"], float("nan"))
+    ws = torch.empty(64 << 20, dtype=torch.uint8, device=d["q"].device)
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        A.forward(*args, out=out, ws=ws, **kw)  # warm-up outside the capture
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        A.forward(*args, out=out, ws=ws, **kw)
+    q0 = d["q"].clone()
+    for rep in range(3):
+        if rep == 2:
+            d["q"].copy_(torch.flip(q0, dims=[0]))  # new inputs, same buffers
+        out.fill_(float("nan"))
+        junk = torch.randn(1 << 20, device=d["q"].device).sum()  # eager work between replays
+        g.replay()
+        torch.cuda.synchronize()
+        got = out.clone()
+        eager = torch.full_like(out, float("nan"))
+        A.forward(*args, out=eager, **kw)
+        torch.cuda.synchronize()
+        assert torch.equal(got, eager), f"replay {rep} differs from eager"
+        if rep < 2:
+            compare(case, got.float().cpu().numpy().astype(np.float64), ref,
+                    label=f"graph replay {rep}")
+        assert torch.isfinite(junk)
+
+
 def test_two_streams_separate_workspaces():
     import paged_varlen_attention_ua_amd.attention as A
     c1, r1, _ = _workload("long_decode_bf16_d128_32q8kv_w4096")
