@@ -186,9 +186,6 @@ Params make_params(const ua_problem* p, const ua_plan_t* plan, const ua_args* a,
   q.block_q = plan->block_q;
   q.n_part = plan->n_part;
   q.window = p->window > 0 ? p->window : 0;
-  int trips = 0;
-  while ((1 << trips) < p->num_seqs + 1) ++trips;
-  q.search_trips = trips;
   const bool fp8 = is_fp8(p->kv_dtype);
   // e4m3fnuz codes are decoded to twice their value: halve both factors.
   const double half = p->kv_dtype == UA_FP8_E4M3FNUZ ? 0.5 : 1.0;
@@ -201,7 +198,6 @@ Params make_params(const ua_problem* p, const ua_plan_t* plan, const ua_args* a,
     q.cap_out2 = (float)((double)p->softcap * log2e);
   }
   q.v_scale = fp8 ? (float)((double)p->v_scale * half) : 1.0f;
-  q.grid_x = plan->grid_x;
   q.seq_blocks = plan->flags & 1;
   return q;
 }

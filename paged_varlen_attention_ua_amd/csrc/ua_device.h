@@ -57,19 +57,6 @@ __device__ __forceinline__ uint32_t pack2(float a, float b) {
   }
 }
 
-// acc + both values of a packed QT pair (one dot2 with (1, 1); the products
-// are exact and the sum is accumulated in fp32).
-template <int QT>
-__device__ __forceinline__ float sum2(uint32_t v, float acc) {
-  if constexpr (QT == UA_F16) {
-    return __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, v),
-                                  f16x2{(_Float16)1.0f, (_Float16)1.0f}, acc, false);
-  } else {
-    return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, v),
-                                           bf16x2{(__bf16)1.0f, (__bf16)1.0f}, acc, false);
-  }
-}
-
 // Low / high 16-bit value of a packed pair back to fp32 (exact).
 template <int QT>
 __device__ __forceinline__ float lo16(uint32_t v) {
@@ -171,11 +158,6 @@ __device__ __forceinline__ float wave_max_xor(float v, int mask) {
 }
 __device__ __forceinline__ float wave_sum_xor(float v, int mask) {
   return v + __shfl_xor(v, mask, 64);
-}
-
-template <typename T>
-__device__ __forceinline__ T ld_global(const void* base, int64_t byte_off) {
-  return *reinterpret_cast<const T*>(reinterpret_cast<const char*>(base) + byte_off);
 }
 
 }  // namespace ua

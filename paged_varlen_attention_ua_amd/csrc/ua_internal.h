@@ -15,8 +15,6 @@ constexpr int kLargeRows = 128;
 constexpr int kLarge8Rows = 256;
 // Keys per inner tile of the small-block kernel (two 16-key MFMA blocks).
 constexpr int kSmallTile = 32;
-// Keys per inner tile of the large-block kernel.
-constexpr int kLargeTile = 64;
 // Waves per small-block workgroup; they split the key range of one block.
 constexpr int kSmallWaves = 4;
 
@@ -71,7 +69,6 @@ struct Params {
   int32_t block_q;      // query tokens per query block
   int32_t n_part;       // partitions (1 = one pass)
   int32_t window;       // <= 0: off
-  int32_t search_trips; // ceil(log2(num_seqs + 1))
   float qk_scale2;      // scale * kf * log2(e): raw dot -> base-2 logit
   float cap_in;         // scale * kf / softcap (softcap on)
   float cap_out2;       // softcap * log2(e)
@@ -79,7 +76,6 @@ struct Params {
   // kf, vf: the per-tensor k_scale / v_scale for fp8 caches (1 otherwise),
   // halved for e4m3fnuz, whose codes the kernels decode to twice their value.
   int32_t softcap_on;
-  int32_t grid_x;       // number of query-block slots launched along x
   int32_t seq_blocks;   // 1: block x is the sequence index (every query run fits one block)
   int32_t qq_stride;    // QQ-bias row stride (elements)
   int32_t head_groups;  // blocks per kv head along y (small kernel; 1 otherwise)

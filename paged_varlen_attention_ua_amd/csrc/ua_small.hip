@@ -13,7 +13,7 @@
 // form of the RocKE README, "Why three tables"); otherwise it writes the
 // partition's (m, l, acc) for ua_reduce.
 //
-// Data flow per 32-key tile and wave (no LDS in the loop):
+// Data flow per 32-key tile and wave (K/V data never pass through LDS):
 //   * K rows go straight from HBM into registers already in the MFMA A-operand
 //     layout (lane l: key key_of_row(l % 16)), and S^T = K Q^T comes out with
 //     one query row per lane (row = l % 16).
@@ -520,9 +520,9 @@ __global__ __launch_bounds__(64 * kSmallWaves, 2) void small_kernel(Params p) {
       oacc[c] = mfma16<QT>(v_operand<QT, FP8, D, FNUZ>(t, c), pb, oacc[c]);
   };
 
-  // One tile per wave in flight; latency is hidden by running three waves per
-  // SIMD (measured faster on MI355X than a two-tile register pipeline, whose
-  // register pressure made the allocator reuse registers with loads in flight).
+  // Tile loop.  Paged caches with D <= 128 keep two tiles in flight per wave
+  // (the partial first and last tiles are peeled off so that the interior
+  // loop carries no clamping); otherwise one tile at a time.
   if constexpr (PAGE16 && D <= 128) {
     // Only a wave's first tile (partition or window start) and last tile
     // (partition end) can be partial; the interior tiles run two deep: the
@@ -575,56 +575,7 @@ __global__ __launch_bounds__(64 * kSmallWaves, 2) void small_kernel(Params p) {
   float l_row = wave_sum_xor(l_run, 16);
   l_row = wave_sum_xor(l_row, 32);
 
-  if constexpr (kSmallWaves == 1) {
-    // One wave: write straight from registers.  O^T accumulator register
-    // (c, r) holds O[row l%16][D/4*g + E*r + c].
-    if (!row_ok) return;
-    const int tok = tok0 + rt;
-    const int64_t rrow = (int64_t)tok * p.num_q_heads + h;
-    if constexpr (SPLIT) {
-      if (g == 0) {
-        p.ws_m[(int64_t)part * R + rrow] = m_run;
-        p.ws_l[(int64_t)part * R + rrow] = l_row;
-      }
-      float* dst = p.ws_acc + ((int64_t)part * R + rrow) * D + DQ * g;
-#pragma unroll
-      for (int r = 0; r < 4; ++r)
-#pragma unroll
-        for (int c = 0; c < E; c += 4)
-          *reinterpret_cast<f32x4*>(dst + E * r + c) =
-              f32x4{oacc[c][r], oacc[c + 1][r], oacc[c + 2][r], oacc[c + 3][r]};
-    } else {
-      const float sink2 = p.sinks != nullptr ? p.sinks[h] * kLog2e : -INFINITY;
-      const float Mt = fmaxf(m_run, sink2);
-      const float Ms = (Mt == -INFINITY) ? 0.0f : Mt;
-      const float f = fast_exp2(m_run - Ms);
-      float L = l_row * f;
-      const bool any_key = L > 0.0f;
-      if (sink2 != -INFINITY) L += fast_exp2(sink2 - Ms);
-      const float inv = any_key ? p.v_scale * f / L : 0.0f;
-      char* dst = reinterpret_cast<char*>(p.out) +
-                  ((int64_t)tok * p.o_stride_tok + (int64_t)h * p.o_stride_head + DQ * g) * 2;
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        uint32_t packed[E / 2];
-#pragma unroll
-        for (int c = 0; c < E; c += 2) packed[c / 2] = pack2<QT>(oacc[c][r] * inv, oacc[c + 1][r] * inv);
-        if constexpr (E == 8) {
-          *reinterpret_cast<u32x4*>(dst + 2 * E * r) = u32x4{packed[0], packed[1], packed[2], packed[3]};
-        } else if constexpr (E == 16) {
-          *reinterpret_cast<u32x4*>(dst + 2 * E * r) = u32x4{packed[0], packed[1], packed[2], packed[3]};
-          *reinterpret_cast<u32x4*>(dst + 2 * E * r + 16) =
-              u32x4{packed[4], packed[5], packed[6], packed[7]};
-        } else {
-          *reinterpret_cast<u32x2*>(dst + 2 * E * r) = u32x2{packed[0], packed[1]};
-        }
-      }
-      if (p.lse != nullptr && g == 0)
-        p.lse[rrow] = (L > 0.0f) ? (Ms + fast_log2(L)) * kLn2 : -INFINITY;
-    }
-    return;
-  } else {
-  // Several waves: merge their states through LDS.
+  // Merge the waves' states through LDS.
   if (g == 0) {
     sm_m[wave][r16] = m_run;
     sm_l[wave][r16] = l_row;
@@ -696,7 +647,6 @@ __global__ __launch_bounds__(64 * kSmallWaves, 2) void small_kernel(Params p) {
       if (p.lse != nullptr && chunk == 0)
         p.lse[rrow] = (L > 0.0f) ? (Ms + fast_log2(L)) * kLn2 : -INFINITY;
     }
-  }
   }
 }
 
