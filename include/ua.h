@@ -45,7 +45,8 @@
  * data preconditions are NOT checked: 0 <= q_len <= kv_len <= max_seqlen_k,
  * q_len <= max_seqlen_q, non-decreasing cu_seqlens_q with cu_seqlens_q[0] = 0
  * and cu_seqlens_q[num_seqs] = total_q, block-table entries in [0, num_blocks)
- * for every block a sequence uses.  Violating them is undefined behaviour.
+ * for every block a sequence uses.  Violating them is undefined behaviour;
+ * ua_check_inputs checks them on the device without faulting (debugging aid).
  */
 #ifndef UA_H
 #define UA_H
@@ -57,7 +58,7 @@
 extern "C" {
 #endif
 
-#define UA_ABI_VERSION 3
+#define UA_ABI_VERSION 4
 
 /* UA_FP8_E4M3FN: OCP E4M3 (bias 7, max 448, no inf, NaN = S.1111.111).
  * UA_FP8_E4M3FNUZ: E4M3 with bias 8 (max 240, no inf, no -0, NaN = 0x80). */
@@ -207,6 +208,27 @@ uint64_t ua_workspace_acc_offset(const ua_problem* prob, const ua_plan_t* plan);
 
 /* Static string for a status code. */
 const char* ua_status_string(int32_t status);
+
+/* Violation bits written by ua_check_inputs. */
+#define UA_CHECK_CU 1     /* cu_seqlens_q[0] != 0, decreasing, or last != total_q */
+#define UA_CHECK_QLEN 2   /* some q_len > max_seqlen_q */
+#define UA_CHECK_KVLEN 4  /* some kv_len < 0, < q_len or > max_seqlen_k */
+#define UA_CHECK_BLOCK 8  /* a block-table entry a sequence uses is outside [0, num_blocks) */
+
+/*
+ * ua_check_inputs: debugging aid for the device-side data preconditions the
+ * forward entry points do not check (see "Errors" above).  Launches one small
+ * workgroup on `stream` that reads cu_seqlens_q, seq_lens and, per sequence,
+ * the first ceil(kv_len / block_size) block-table entries (kv_len clamped to
+ * the row), and stores the OR of the UA_CHECK_* bits that apply (0: all
+ * preconditions hold) to flags[0], a caller-owned device int32.  Reads stay
+ * inside the arrays the problem sizes, whatever their contents; nothing is
+ * trapped.  The result is valid once the stream reaches the launch.  Returns
+ * UA_EINVAL for an invalid problem or missing pointers, UA_EHIP on a launch
+ * error.
+ */
+ua_status ua_check_inputs(const ua_problem* prob, const ua_args* args, int32_t* flags,
+                          void* stream);
 
 /* UA_ABI_VERSION of the built library. */
 int32_t ua_abi_version(void);

@@ -161,3 +161,20 @@ def forward(q, k_cache, v_cache, block_table, cu_seqlens_q, seq_lens, *, max_seq
         B.ua_forward_splitkv(prob, plan, args, ctypes.c_void_p(ws.data_ptr()), ws.numel(), sp)
         B.ua_reduce(prob, plan, args, ctypes.c_void_p(ws.data_ptr()), ws.numel(), sp)
     return out, plan
+
+
+def check_inputs(q, k_cache, v_cache, block_table, cu_seqlens_q, seq_lens, *, max_seqlen_q,
+                 max_seqlen_k, scale=1.0, k_scale=1.0, v_scale=1.0):
+    """Run ua_check_inputs on the device; returns the set of violated preconditions
+    (names from binding.UA_CHECK_BITS), empty when the inputs are valid."""
+    out = torch.empty_like(q)
+    prob = make_problem(q, k_cache, v_cache, block_table, num_seqs=seq_lens.shape[0],
+                        max_seqlen_q=max_seqlen_q, max_seqlen_k=max_seqlen_k, scale=scale,
+                        k_scale=k_scale, v_scale=v_scale, out=out)
+    args = make_args(q, k_cache, v_cache, block_table, cu_seqlens_q, seq_lens, out)
+    flags = torch.full((1,), -1, dtype=torch.int32, device=q.device)
+    stream = torch.cuda.current_stream(q.device)
+    B.ua_check_inputs(prob, args, ctypes.c_void_p(flags.data_ptr()),
+                      ctypes.c_void_p(stream.cuda_stream))
+    bits = int(flags.item())
+    return {name for bit, name in B.UA_CHECK_BITS.items() if bits & bit}

@@ -15,6 +15,7 @@ LIB_PATH = os.path.join(HERE, "libua.so")
 
 UA_F16, UA_BF16, UA_FP8_E4M3FN, UA_FP8_E4M3FNUZ = 0, 1, 2, 3
 UA_PATH_AUTO, UA_PATH_2D, UA_PATH_SPLITKV = 0, 1, 2
+UA_CHECK_BITS = {1: "cu_seqlens_q", 2: "q_len", 4: "kv_len", 8: "block_table"}
 UA_OK = 0
 
 
@@ -72,7 +73,7 @@ _lib = None
 _lib_lock = threading.Lock()
 
 EXPORTS = ["ua_plan", "ua_forward_2d", "ua_forward_splitkv", "ua_reduce", "ua_forward",
-           "ua_workspace_acc_offset", "ua_status_string", "ua_abi_version"]
+           "ua_workspace_acc_offset", "ua_status_string", "ua_check_inputs", "ua_abi_version"]
 
 
 def lib():
@@ -103,6 +104,9 @@ def lib():
             L.ua_workspace_acc_offset.restype = ctypes.c_uint64
             L.ua_status_string.argtypes = [ctypes.c_int32]
             L.ua_status_string.restype = ctypes.c_char_p
+            L.ua_check_inputs.argtypes = [P(UaProblem), P(UaArgs), ctypes.c_void_p,
+                                          ctypes.c_void_p]
+            L.ua_check_inputs.restype = ctypes.c_int32
             L.ua_abi_version.argtypes = []
             L.ua_abi_version.restype = ctypes.c_int32
             _lib = L
@@ -132,6 +136,11 @@ def ua_forward_splitkv(problem, plan, args, workspace_ptr, workspace_bytes, stre
     _check("ua_forward_splitkv", lib().ua_forward_splitkv(
         ctypes.byref(problem), ctypes.byref(plan), ctypes.byref(args), workspace_ptr,
         workspace_bytes, stream))
+
+
+def ua_check_inputs(problem, args, flags_ptr, stream=None):
+    _check("ua_check_inputs", lib().ua_check_inputs(ctypes.byref(problem), ctypes.byref(args),
+                                                    flags_ptr, stream))
 
 
 def ua_reduce(problem, plan, args, workspace_ptr, workspace_bytes, stream=None):

@@ -22,6 +22,7 @@ SOURCES = [
     ("ua_large.hip", "ua_large_f16.o", ["-DUA_QT=0"]),
     ("ua_large.hip", "ua_large_bf16.o", ["-DUA_QT=1"]),
     ("ua_reduce.hip", "ua_reduce.o", []),
+    ("ua_check.hip", "ua_check.o", []),
 ]
 ARCH = "gfx950"
 

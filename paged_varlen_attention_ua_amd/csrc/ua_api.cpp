@@ -391,6 +391,18 @@ ua_status ua_reduce(const ua_problem* prob, const ua_plan_t* plan, const ua_args
   return e == hipSuccess ? UA_OK : UA_EHIP;
 }
 
+ua_status ua_check_inputs(const ua_problem* prob, const ua_args* args, int32_t* flags,
+                          void* stream) {
+  ua_status st = validate(prob);
+  if (st != UA_OK) return st;
+  if (!args || !flags) return UA_EINVAL;
+  if (prob->num_seqs > 0 && (!args->cu_seqlens_q || !args->seq_lens || !args->block_table))
+    return UA_EINVAL;
+  if (prob->num_seqs == 0 && !args->cu_seqlens_q) return UA_EINVAL;
+  hipError_t e = launch_check(prob, args, flags, (hipStream_t)stream);
+  return e == hipSuccess ? UA_OK : UA_EHIP;
+}
+
 ua_status ua_forward(const ua_problem* prob, const ua_plan_t* plan, const ua_args* args,
                      void* workspace, size_t workspace_bytes, void* stream) {
   if (!plan) return UA_EINVAL;

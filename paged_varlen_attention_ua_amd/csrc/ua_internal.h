@@ -108,5 +108,7 @@ inline hipError_t launch_large(const Params& p, int q_dtype, int kv_fmt, int hea
              : launch_large_bf16(p, kv_fmt, head_dim, split, eight_waves, grid, stream);
 }
 hipError_t launch_reduce(const Params& p, int o_dtype, int head_dim, hipStream_t stream);
+hipError_t launch_check(const ua_problem* p, const ua_args* a, int32_t* flags,
+                        hipStream_t stream);
 
 }  // namespace ua

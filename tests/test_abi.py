@@ -33,7 +33,7 @@ def test_library_exports_every_declared_symbol():
     lib = ctypes.CDLL(B.LIB_PATH)
     for fn in _declared_functions():
         assert hasattr(lib, fn), fn
-    assert U.ua_abi_version() == 3
+    assert U.ua_abi_version() == 4
 
 
 def test_struct_sizes_match_header_layout():
@@ -193,6 +193,16 @@ def test_forward_rejects_mismatched_plan_and_missing_workspace():
                                       ctypes.c_void_p(1 << 21), 16, None) == -3
     assert B.lib().ua_reduce(ctypes.byref(p), ctypes.byref(plan), ctypes.byref(args),
                              None, 0, None) == -3
+
+
+def test_check_inputs_rejects_missing_pointers():
+    p = problem()
+    args = B.UaArgs()
+    assert B.lib().ua_check_inputs(ctypes.byref(p), ctypes.byref(args), None, None) == -1
+    assert B.lib().ua_check_inputs(ctypes.byref(p), ctypes.byref(args),
+                                   ctypes.c_void_p(1 << 20), None) == -1
+    assert B.lib().ua_check_inputs(ctypes.byref(problem(head_dim=96)), ctypes.byref(args),
+                                   ctypes.c_void_p(1 << 20), None) == -2
 
 
 def test_empty_batch_is_a_no_op():

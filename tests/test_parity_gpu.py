@@ -387,6 +387,37 @@ def test_graph_capture_replays(path, n_part):
         assert torch.isfinite(junk)
 
 
+def test_check_inputs_reports_each_violation():
+    """ua_check_inputs: valid inputs give no bits; each broken precondition sets
+    its bit (the forward is never run on the broken inputs)."""
+    import paged_varlen_attention_ua_amd.attention as A
+    base = make_case(seqs=MIXED_SEQS, seed=140, **BASE)
+
+    def check(case, **over):
+        d = to_device(case)
+        kw = dict(max_seqlen_q=case["max_seqlen_q"], max_seqlen_k=case["max_seqlen_k"])
+        kw.update(over)
+        return A.check_inputs(d["q"], d["k_cache"], d["v_cache"], d["block_table"],
+                              d["cu_seqlens_q"], d["seq_lens"], **kw)
+
+    assert check(base) == set()
+    c = dict(base, cu_seqlens_q=base["cu_seqlens_q"].copy())
+    c["cu_seqlens_q"][2] = c["cu_seqlens_q"][1] - 1
+    assert "cu_seqlens_q" in check(c)
+    assert check(base, max_seqlen_q=base["max_seqlen_q"] - 1) == {"q_len"}
+    c = dict(base, seq_lens=base["seq_lens"].copy())
+    c["seq_lens"][1] = 16  # sequence 1 has 17 queries
+    assert check(c) == {"kv_len"}
+    assert check(base, max_seqlen_k=base["max_seqlen_k"] - 1) == {"kv_len"}
+    for bad in (base["k_cache"].shape[0], -1):
+        c = dict(base, block_table=base["block_table"].copy())
+        c["block_table"][5, 2] = bad  # a block sequence 5 (700 keys) uses
+        assert check(c) == {"block_table"}
+    c = dict(base, block_table=base["block_table"].copy())
+    c["block_table"][0, -1] = -7  # padding column: not used by any sequence
+    assert check(c) == set()
+
+
 def test_two_streams_separate_workspaces():
     import paged_varlen_attention_ua_amd.attention as A
     c1, r1, _ = _workload("long_decode_bf16_d128_32q8kv_w4096")
