@@ -230,10 +230,15 @@ def time_case(case, steps, warmup, path="auto", n_part=0, touched=None, kernel_e
                 n_part=int(plan.n_part), rotation_sets=R, kernel=int(plan.kernel))
 
 
+# Sources that decide the decode partition kernel's memory traffic: the kernel,
+# its helpers and the planner that picks its partitioning.
+TRAFFIC_SOURCES = ("ua_small.hip", "ua_device.h", "ua_internal.h", "ua_api.cpp")
+
+
 def kernel_source_digest():
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "paged_varlen_attention_ua_amd", "csrc")
-    for f in sorted(os.listdir(csrc)):
+    for f in TRAFFIC_SOURCES:
         h.update(open(os.path.join(csrc, f), "rb").read())
     return h.hexdigest()[:16]
 
