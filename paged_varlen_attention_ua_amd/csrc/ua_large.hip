@@ -19,9 +19,10 @@
 //   * online softmax in the base-2 domain (README section "2D vs 2D") on the
 //     raw dot products (the logit scale is applied inside the one FMA that
 //     feeds exp2), with the running maximum only moved when a tile's maximum
-//     exceeds it by more than 2^8 (exact up to rounding: every key of a row is
-//     scaled by the same maximum between moves, and p <= 256 stays
-//     representable);
+//     exceeds it by more than 8 (exact up to rounding: every key of a row is
+//     scaled by the same maximum between moves, and p <= 2^8 stays
+//     representable); p is formed against the running maximum first and the
+//     tile maximum is only taken when a lane's sum of p exceeds 2^8;
 //   * causal, window and range masks are applied only on tiles that need them
 //     (the mask-phase split of the README's "BLOCK_M=128" section);
 //   * O^T = V^T P^T on 32x32x16 MFMA: P^T is already the B operand in the
@@ -54,6 +55,34 @@ __device__ __forceinline__ u32x2 lds_read_tr16(const char* p) {
 #else
   (void)p;
   return u32x2{0, 0};
+#endif
+}
+
+// The same read at a 32-bit LDS byte address.
+__device__ __forceinline__ u32x2 lds_read_tr16_at(uint32_t a) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+  s16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(uintptr_t)a);
+  return __builtin_bit_cast(u32x2, v);
+#else
+  (void)a;
+  return u32x2{0, 0};
+#endif
+}
+
+// LDS byte address of buffer p plus off, formed by one VALU add where it is
+// written (so the compiler neither keeps a copy per buffer live across the
+// loop nor splits it into one add per immediate offset).
+__device__ __forceinline__ uint32_t lds_offset_add(const char* p, int off) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  const uint32_t base =
+      (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) char*)(p);
+  uint32_t r;
+  asm volatile("v_add_u32 %0, %1, %2" : "=v"(r) : "s"(base), "v"(off));
+  return r;
+#else
+  (void)p;
+  return (uint32_t)off;
 #endif
 }
 
@@ -167,6 +196,7 @@ __global__ __launch_bounds__(64 * NW, (large_min_groups<D, NW>())) void large_ke
   // tiles before it is used; otherwise two deep (measured on MI355X: four deep
   // is 2-4% faster for eight-wave groups and 7% slower for D = 256).
   constexpr int NBUF = (!FP8 && NW == 8) ? 4 : 2;
+  constexpr bool kLazyMax = NW == 8;
   constexpr int TB2 = NBUF > 2 ? C::TILEB : 16;
   __shared__ __attribute__((aligned(1024))) char sK0[C::TILEB];
   __shared__ __attribute__((aligned(1024))) char sK1[C::TILEB];
@@ -418,25 +448,47 @@ __global__ __launch_bounds__(64 * NW, (large_min_groups<D, NW>())) void large_ke
       __attribute__((always_inline)) {
     // ---- S^T = K Q^T
     f32x16 sacc[C::KB];
+    if constexpr (NW == 8) {
+      // Eight-wave groups: the scheduling-group hint below is not honoured
+      // here (the reads landed right before their MFMAs), so the order is
+      // pinned: K reads run four MFMAs ahead.
+      constexpr int NQ = C::KB * C::QC;
+      constexpr int LEAD = 4;
+      u32x4 kr[NQ];
 #pragma unroll
-    for (int kb = 0; kb < C::KB; ++kb) {
-      sacc[kb] = f32x16{};
+      for (int i = 0; i < LEAD; ++i)
+        kr[i] = *reinterpret_cast<const u32x4*>(sk + 32 * (i / C::QC) * ROWB + kaddr[i % C::QC]);
 #pragma unroll
-      for (int c = 0; c < C::QC; ++c) {
-        const u32x4 a = *reinterpret_cast<const u32x4*>(sk + 32 * kb * ROWB + kaddr[c]);
-        sacc[kb] = mfma32<QT>(a, qop[c], sacc[kb]);
+      for (int i = 0; i < NQ; ++i) {
+        if (i + LEAD < NQ) {
+          const int j = i + LEAD;
+          kr[j] = *reinterpret_cast<const u32x4*>(sk + 32 * (j / C::QC) * ROWB + kaddr[j % C::QC]);
+        }
+        const int kb = i / C::QC, c = i % C::QC;
+        sacc[kb] = mfma32<QT>(kr[i], qop[c], c == 0 ? f32x16{} : sacc[kb]);
+        __builtin_amdgcn_sched_barrier(0);
       }
-    }
-    // Schedule: keep four K reads in flight ahead of the QK MFMAs (the default
-    // schedule issued them two MFMAs ahead, exposing LDS latency; measured on
-    // MI355X: 9% faster for D = 256, neutral for D <= 128).
-    __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);  // DS reads
+    } else {
 #pragma unroll
-    for (int k = 0; k < C::KB * C::QC - 4; ++k) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
-      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      for (int kb = 0; kb < C::KB; ++kb) {
+        sacc[kb] = f32x16{};
+#pragma unroll
+        for (int c = 0; c < C::QC; ++c) {
+          const u32x4 a = *reinterpret_cast<const u32x4*>(sk + 32 * kb * ROWB + kaddr[c]);
+          sacc[kb] = mfma32<QT>(a, qop[c], sacc[kb]);
+        }
+      }
+      // Schedule: keep four K reads in flight ahead of the QK MFMAs (the
+      // default schedule issued them two MFMAs ahead, exposing LDS latency;
+      // measured on MI355X: 9% faster for D = 256).
+      __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);  // DS reads
+#pragma unroll
+      for (int k = 0; k < C::KB * C::QC - 4; ++k) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      }
+      __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
     }
-    __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
     // Per-token K scales: registers 4j .. 4j + 3 of block kb are keys
     // 32 kb + 8 j + 4 g2 + 0..3 of the tile.
     if constexpr (tsc) {
@@ -510,56 +562,142 @@ __global__ __launch_bounds__(64 * NW, (large_min_groups<D, NW>())) void large_ke
           sacc[kb][r] = (uint32_t)(kd0 + o) < span ? sacc[kb][r] : -INFINITY;
         }
     }
-    float mt = -INFINITY;
+    // ---- P = 2^(s * cs - m), packed as the B operands of the PV MFMAs.
+    // Eight-wave blocks (kLazyMax) form P against the running maximum m
+    // first; the tile's own maximum is only needed
+    // when m must move, i.e. when some p of the tile exceeds 2^8 (then the sum
+    // of the lane's p exceeds 2^8 too) or the row has no maximum yet and sees
+    // keys of this tile (its p were formed against 0 and may all have
+    // underflowed); when no lane of the wave sees either, the rule "move m
+    // when the tile's maximum exceeds it by more than 8" would not move it
+    // (up to the rounding of exp2), so the tile maximum is skipped.  This
+    // puts a branch between the exp2s and the PV MFMAs, which a second wave
+    // on the SIMD covers: measured on MI355X, 2-4% faster with eight waves
+    // (head dim <= 128) and 5-11% slower with four (head dim 64 and 256).
+    u32x4 pop[TK / 16];
+    float psum;
+    auto make_p = [&]() __attribute__((always_inline)) {
+      const float m_use = (m_run == -INFINITY) ? 0.0f : m_run;
+      float ps = 0.0f;
 #pragma unroll
-    for (int kb = 0; kb < C::KB; ++kb)
+      for (int kk = 0; kk < TK / 16; ++kk) {
+        // V scales of this operand's keys 16 kk + 4 g2 + {0..3, 8..11} (q = 0..3).
+        f32x4 v4[2] = {f32x4{1.f, 1.f, 1.f, 1.f}, f32x4{1.f, 1.f, 1.f, 1.f}};
+        if constexpr (tsc) {
+          v4[0] = *reinterpret_cast<const f32x4*>(sc + TK + 16 * kk + 4 * g2);
+          v4[1] = *reinterpret_cast<const f32x4*>(sc + TK + 16 * kk + 4 * g2 + 8);
+        }
 #pragma unroll
-      for (int r = 0; r < 16; ++r) mt = fmaxf(mt, sacc[kb][r]);
-    // Row maximum across the lane pair (l, l ^ 32) holding the same row,
-    // in base-2 logit units (cs > 0, and -inf stays -inf).
-    mt = wave_max_xor(mt, 32) * cs;
-    // Move the running maximum only when this tile exceeds it by > 8 (base 2).
-    const bool need = mt > m_run + 8.0f;
-    if (__builtin_amdgcn_ballot_w64(need)) {
+        for (int q = 0; q < 4; ++q) {
+          const float a =
+              fast_exp2(__builtin_fmaf(sacc[kk >> 1][8 * (kk & 1) + 2 * q], cs, -m_use));
+          const float b =
+              fast_exp2(__builtin_fmaf(sacc[kk >> 1][8 * (kk & 1) + 2 * q + 1], cs, -m_use));
+          // The row sum is of the fp32 p (per-token V scales excluded).  One
+          // accumulator: head dim 256 runs at the register limit, where a
+          // second one cost the K reads their lead over the QK MFMAs.
+          ps += a + b;
+          if constexpr (tsc)
+            pop[kk][q] = pack2<QT>(a * v4[q >> 1][2 * (q & 1)], b * v4[q >> 1][2 * (q & 1) + 1]);
+          else
+            pop[kk][q] = pack2<QT>(a, b);
+        }
+      }
+      psum = ps;
+    };
+    // Tile maximum (across the lane pair (l, l ^ 32) holding the same row, in
+    // base-2 logit units: cs > 0, and -inf stays -inf); m moves to it when it
+    // exceeds m by more than 8.  Returns whether any row of the wave moved.
+    auto move_max = [&]() __attribute__((always_inline)) -> bool {
+      float mt = -INFINITY;
+#pragma unroll
+      for (int kb = 0; kb < C::KB; ++kb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) mt = fmaxf(mt, sacc[kb][r]);
+      mt = wave_max_xor(mt, 32) * cs;
+      const bool need = mt > m_run + 8.0f;
+      if (!__builtin_amdgcn_ballot_w64(need)) return false;
       const float m_new = need ? mt : m_run;
       const float alpha = need ? fast_exp2(m_run - m_new) : 1.0f;  // m_run = -inf -> 0
       l_run *= alpha;
 #pragma unroll
       for (int d = 0; d < C::DB; ++d) oacc[d] *= alpha;
       m_run = m_new;
-    }
-    const float m_use = (m_run == -INFINITY) ? 0.0f : m_run;
-    // ---- P = 2^(s * cs - m), packed as the B operands of the PV MFMAs
-    u32x4 pop[TK / 16];
-    float psum = 0.0f;
+      return true;
+    };
+    if constexpr (kLazyMax) {
+      make_p();
+      const bool first = m_run == -INFINITY && max(kt, row_lo) < min(kt + TK, row_hi);
+      if (__builtin_amdgcn_ballot_w64(!(psum <= 256.0f) || first))
+        if (move_max()) make_p();
+    } else {
+      // Written out rather than through the lambdas: head dim 256 runs at the
+      // register limit, and the lambda form cost the K reads their lead over
+      // the QK MFMAs there.
+      float mt = -INFINITY;
 #pragma unroll
-    for (int kk = 0; kk < TK / 16; ++kk) {
-      // V scales of this operand's keys 16 kk + 4 g2 + {0..3, 8..11} (q = 0..3).
-      f32x4 v4[2] = {f32x4{1.f, 1.f, 1.f, 1.f}, f32x4{1.f, 1.f, 1.f, 1.f}};
-      if constexpr (tsc) {
-        v4[0] = *reinterpret_cast<const f32x4*>(sc + TK + 16 * kk + 4 * g2);
-        v4[1] = *reinterpret_cast<const f32x4*>(sc + TK + 16 * kk + 4 * g2 + 8);
+      for (int kb = 0; kb < C::KB; ++kb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) mt = fmaxf(mt, sacc[kb][r]);
+      mt = wave_max_xor(mt, 32) * cs;
+      const bool need = mt > m_run + 8.0f;
+      if (__builtin_amdgcn_ballot_w64(need)) {
+        const float m_new = need ? mt : m_run;
+        const float alpha = need ? fast_exp2(m_run - m_new) : 1.0f;  // m_run = -inf -> 0
+        l_run *= alpha;
+#pragma unroll
+        for (int d = 0; d < C::DB; ++d) oacc[d] *= alpha;
+        m_run = m_new;
       }
+      const float m_use = (m_run == -INFINITY) ? 0.0f : m_run;
+      psum = 0.0f;
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const float a = fast_exp2(__builtin_fmaf(sacc[kk >> 1][8 * (kk & 1) + 2 * q], cs, -m_use));
-        const float b =
-            fast_exp2(__builtin_fmaf(sacc[kk >> 1][8 * (kk & 1) + 2 * q + 1], cs, -m_use));
-        psum += a + b;
-        if constexpr (tsc)
-          pop[kk][q] = pack2<QT>(a * v4[q >> 1][2 * (q & 1)], b * v4[q >> 1][2 * (q & 1) + 1]);
-        else
-          pop[kk][q] = pack2<QT>(a, b);
+      for (int kk = 0; kk < TK / 16; ++kk) {
+        f32x4 v4[2] = {f32x4{1.f, 1.f, 1.f, 1.f}, f32x4{1.f, 1.f, 1.f, 1.f}};
+        if constexpr (tsc) {
+          v4[0] = *reinterpret_cast<const f32x4*>(sc + TK + 16 * kk + 4 * g2);
+          v4[1] = *reinterpret_cast<const f32x4*>(sc + TK + 16 * kk + 4 * g2 + 8);
+        }
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const float a =
+              fast_exp2(__builtin_fmaf(sacc[kk >> 1][8 * (kk & 1) + 2 * q], cs, -m_use));
+          const float b =
+              fast_exp2(__builtin_fmaf(sacc[kk >> 1][8 * (kk & 1) + 2 * q + 1], cs, -m_use));
+          psum += a + b;
+          if constexpr (tsc)
+            pop[kk][q] = pack2<QT>(a * v4[q >> 1][2 * (q & 1)], b * v4[q >> 1][2 * (q & 1) + 1]);
+          else
+            pop[kk][q] = pack2<QT>(a, b);
+        }
       }
     }
     l_run += psum;
     // ---- O^T += V^T P^T
+    // With a ring of more than 64 KB the V buffers lie beyond the reads'
+    // 16-bit immediate offset: then the buffer base goes into the address
+    // register with one add per read address and tile (the compiler's own
+    // form took one per read), and only 16 kk rows stay immediate.
+    constexpr bool kVHigh = 2 * NBUF * C::TILEB > 65536;
+    uint32_t vb[2][C::DB];
+    if constexpr (kVHigh) {
+#pragma unroll
+      for (int hh = 0; hh < 2; ++hh)
+#pragma unroll
+        for (int d = 0; d < C::DB; ++d) vb[hh][d] = lds_offset_add(sv, vaddr[hh][d]);
+    }
 #pragma unroll
     for (int d = 0; d < C::DB; ++d) {
 #pragma unroll
       for (int kk = 0; kk < TK / 16; ++kk) {
-        const u32x2 lo2 = lds_read_tr16(sv + 16 * kk * ROWB + vaddr[0][d]);
-        const u32x2 hi2 = lds_read_tr16(sv + 16 * kk * ROWB + vaddr[1][d]);
+        u32x2 lo2, hi2;
+        if constexpr (kVHigh) {
+          lo2 = lds_read_tr16_at(vb[0][d] + 16 * kk * ROWB);
+          hi2 = lds_read_tr16_at(vb[1][d] + 16 * kk * ROWB);
+        } else {
+          lo2 = lds_read_tr16(sv + 16 * kk * ROWB + vaddr[0][d]);
+          hi2 = lds_read_tr16(sv + 16 * kk * ROWB + vaddr[1][d]);
+        }
         oacc[d] = mfma32<QT>(u32x4{lo2[0], lo2[1], hi2[0], hi2[1]}, pop[kk], oacc[d]);
       }
     }
