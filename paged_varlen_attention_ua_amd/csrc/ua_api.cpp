@@ -257,8 +257,11 @@ ua_status ua_plan(const ua_problem* prob, int32_t num_cus, int32_t force_path,
   int64_t eff_k = prob->max_seqlen_k;
   if (prob->window > 0)
     eff_k = std::min<int64_t>(eff_k, (int64_t)prob->window + prob->max_seqlen_q - 1);
+  // The eight-wave kernel has no softcap / ALiBi / QQ-bias path.
+  const bool plain_logits = !(prob->softcap > 0.f) && !prob->has_alibi && !prob->has_qq_bias;
   const bool eight = !small && prob->head_dim <= 128 && is_16bit(prob->kv_dtype) &&
-                     (int64_t)prob->max_seqlen_q * G >= kLarge8Rows && eff_k >= 4096;
+                     plain_logits && (int64_t)prob->max_seqlen_q * G >= kLarge8Rows &&
+                     eff_k >= 4096;
   plan->kernel = small ? 0 : (eight ? 2 : 1);
   plan->block_q = small ? kSmallRows / Gs : (eight ? kLarge8Rows : kLargeRows) / G;
   const int bq = plan->block_q;

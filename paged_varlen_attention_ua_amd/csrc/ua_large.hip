@@ -197,15 +197,10 @@ __global__ __launch_bounds__(64 * NW, (large_min_groups<D, NW>())) void large_ke
   // is 2-4% faster for eight-wave groups and 7% slower for D = 256).
   constexpr int NBUF = (!FP8 && NW == 8) ? 4 : 2;
   constexpr bool kLazyMax = NW == 8;
-  constexpr int TB2 = NBUF > 2 ? C::TILEB : 16;
-  __shared__ __attribute__((aligned(1024))) char sK0[C::TILEB];
-  __shared__ __attribute__((aligned(1024))) char sK1[C::TILEB];
-  __shared__ __attribute__((aligned(1024))) char sK2[TB2];
-  __shared__ __attribute__((aligned(1024))) char sK3[TB2];
-  __shared__ __attribute__((aligned(1024))) char sV0[C::TILEB];
-  __shared__ __attribute__((aligned(1024))) char sV1[C::TILEB];
-  __shared__ __attribute__((aligned(1024))) char sV2[TB2];
-  __shared__ __attribute__((aligned(1024))) char sV3[TB2];
+  constexpr bool kPingPong = NW == 8 && !FP8;
+  // Ring buffers: K of slot b at sRing + b * TILEB, V at sRing + (NBUF + b) * TILEB.
+  __shared__ __attribute__((aligned(1024))) char sRing[2 * NBUF * C::TILEB];
+  char* const sK0 = sRing;
   // Row-offset table of tile t in slot t % NBUF.
   __shared__ int64_t sTab[NBUF][TK];
   __shared__ int32_t sm_pg[C::MAXPG];
@@ -282,7 +277,9 @@ __global__ __launch_bounds__(64 * NW, (large_min_groups<D, NW>())) void large_ke
   const int row_lo = p.window > 0 ? max(kl, pos - p.window + 1) : kl;
   const int row_hi = min(k1, pos + 1);
   const float slope2 = (p.alibi != nullptr && row_ok) ? p.alibi[h] * kLog2e : 0.0f;
-  const bool general = p.softcap_on || p.alibi != nullptr || p.qq_bias != nullptr;
+  // Softcap, ALiBi and QQ-bias (not in eight-wave groups, whose launcher
+  // refuses them).
+  const bool general = NW == 4 && (p.softcap_on || p.alibi != nullptr || p.qq_bias != nullptr);
 
   // Q as the B operand of S^T = K Q^T: lane holds Q[row][16c + 8*g2 .. + 8].
   u32x4 qop[C::QC];
@@ -444,10 +441,8 @@ __global__ __launch_bounds__(64 * NW, (large_min_groups<D, NW>())) void large_ke
 
   const int ntiles = (k1 - k0 + TK - 1) / TK;
 
-  auto compute = [&](const char* sk, const char* sv, int kt, const float* sc)
-      __attribute__((always_inline)) {
-    // ---- S^T = K Q^T
-    f32x16 sacc[C::KB];
+  // ---- S^T = K Q^T of the tile in LDS buffer sk.
+  auto qk = [&](const char* sk, f32x16* sacc) __attribute__((always_inline)) {
     if constexpr (NW == 8) {
       // Eight-wave groups: the scheduling-group hint below is not honoured
       // here (the reads landed right before their MFMAs), so the order is
@@ -489,6 +484,12 @@ __global__ __launch_bounds__(64 * NW, (large_min_groups<D, NW>())) void large_ke
       }
       __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
     }
+  };
+  // ---- Logits, masks and P of the tile starting at key kt (S^T in sacc):
+  // moves the running maximum and sum (rescaling O when the maximum moves) and
+  // leaves P^T in pop as the B operands of the PV MFMAs.
+  auto smax = [&](f32x16* sacc, int kt, const float* sc, u32x4* pop)
+      __attribute__((always_inline)) {
     // Per-token K scales: registers 4j .. 4j + 3 of block kb are keys
     // 32 kb + 8 j + 4 g2 + 0..3 of the tile.
     if constexpr (tsc) {
@@ -574,7 +575,6 @@ __global__ __launch_bounds__(64 * NW, (large_min_groups<D, NW>())) void large_ke
     // puts a branch between the exp2s and the PV MFMAs, which a second wave
     // on the SIMD covers: measured on MI355X, 2-4% faster with eight waves
     // (head dim <= 128) and 5-11% slower with four (head dim 64 and 256).
-    u32x4 pop[TK / 16];
     float psum;
     auto make_p = [&]() __attribute__((always_inline)) {
       const float m_use = (m_run == -INFINITY) ? 0.0f : m_run;
@@ -673,7 +673,9 @@ __global__ __launch_bounds__(64 * NW, (large_min_groups<D, NW>())) void large_ke
       }
     }
     l_run += psum;
-    // ---- O^T += V^T P^T
+  };
+  // ---- O^T += V^T P^T (V tile in LDS buffer sv).
+  auto pv = [&](const char* sv, const u32x4* pop) __attribute__((always_inline)) {
     // With a ring of more than 64 KB the V buffers lie beyond the reads'
     // 16-bit immediate offset: then the buffer base goes into the address
     // register with one add per read address and tile (the compiler's own
@@ -711,21 +713,23 @@ __global__ __launch_bounds__(64 * NW, (large_min_groups<D, NW>())) void large_ke
     }
     __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
   };
+  auto compute = [&](const char* sk, const char* sv, int kt, const float* sc)
+      __attribute__((always_inline)) {
+    f32x16 sacc[C::KB];
+    u32x4 pop[TK / 16];
+    qk(sk, sacc);
+    smax(sacc, kt, sc, pop);
+    pv(sv, pop);
+  };
 
   // Buffer B of the ring (compile-time B).
   auto kbuf = [&](auto bc) __attribute__((always_inline)) -> char* {
     constexpr int B = decltype(bc)::value % NBUF;
-    if constexpr (B == 0) return sK0;
-    else if constexpr (B == 1) return sK1;
-    else if constexpr (B == 2) return sK2;
-    else return sK3;
+    return sRing + B * C::TILEB;
   };
   auto vbuf = [&](auto bc) __attribute__((always_inline)) -> char* {
     constexpr int B = decltype(bc)::value % NBUF;
-    if constexpr (B == 0) return sV0;
-    else if constexpr (B == 1) return sV1;
-    else if constexpr (B == 2) return sV2;
-    else return sV3;
+    return sRing + (NBUF + B) * C::TILEB;
   };
   using I0 = std::integral_constant<int, 0>;
   using I1 = std::integral_constant<int, 1>;
@@ -743,9 +747,9 @@ __global__ __launch_bounds__(64 * NW, (large_min_groups<D, NW>())) void large_ke
   __syncthreads();
   if constexpr (FP8) {
     stage_load(sTab[0]);
-    stage_store(sK0, sV0);
+    stage_store(kbuf(I0{}), vbuf(I0{}));
   } else {
-    issue_copy(sK0, sV0, sTab[0]);
+    issue_copy(kbuf(I0{}), vbuf(I0{}), sTab[0]);
     if constexpr (NBUF > 2) {
       if (ntiles > 1) issue_copy(kbuf(I1{}), vbuf(I1{}), sTab[1]);
       if (ntiles > 2) issue_copy(kbuf(I2{}), vbuf(I2{}), sTab[2]);
@@ -788,12 +792,103 @@ __global__ __launch_bounds__(64 * NW, (large_min_groups<D, NW>())) void large_ke
     barrier_lds();
   };
   static_assert(NBUF == 2 || NBUF == 4, "ring depth");
-  for (int t = 0; t < ntiles; t += NBUF) {
-    step(I0{}, t);
-    if (t + 1 < ntiles) step(I1{}, t + 1);
-    if constexpr (NBUF > 2) {
-      if (t + 2 < ntiles) step(I2{}, t + 2);
-      if (t + 3 < ntiles) step(I3{}, t + 3);
+  if constexpr (kPingPong) {
+    // Eight-wave groups on 16-bit caches run as two halves, waves 0-3 (A) and
+    // 4-7 (B), one of each on every SIMD, half a tile apart: between two
+    // barriers one half runs MFMAs (PV of tile t, then QK of tile t + 1)
+    // while the other runs the softmax VALU work of its tile, and the next
+    // interval they swap, so each SIMD's matrix and vector pipes work at the
+    // same time instead of both waves taking turns on one of them.
+    //   interval 0:        A: QK(0), softmax(0)       B: QK(0)
+    //   interval 2t + 1:   A: PV(t), QK(t + 1)        B: softmax(t)
+    //   interval 2t + 2:   A: softmax(t + 1)          B: PV(t), QK(t + 1)
+    // Every wave passes the same barriers (none inside the group branches).
+    // Ring (four deep): the copy of tile t + 3 is issued at interval 2t + 1
+    // into the slot of tile t - 1, whose K was last read at interval 2t - 2
+    // and V at 2t; tile j is waited for at the end of interval 2j - 2, before
+    // its K is first read at 2j - 1 (tile j + 1 stays in flight).  The table
+    // of tile t + 4 is filled at interval 2t + 1 into the slot tile t was
+    // copied with; the copy that reads it is issued at interval 2t + 3.
+    const int grp = wave >> 2;
+    auto kslot = [&](int t) __attribute__((always_inline)) -> char* {
+      return sRing + (t & 3) * C::TILEB;
+    };
+    auto vslot = [&](int t) __attribute__((always_inline)) -> char* {
+      return sRing + (4 + (t & 3)) * C::TILEB;
+    };
+    // Interval i starts with the copy of tile (i + 5) / 2 and the table of
+    // tile (i + 7) / 2 (odd i) and ends, before its barrier, with the wait for
+    // tile i / 2 + 1 (even i).
+    auto start_interval = [&](int i) __attribute__((always_inline)) {
+      if (i & 1) {
+        const int t = (i - 1) >> 1;
+        if (t + 3 < ntiles) issue_copy(kslot(t + 3), vslot(t + 3), sTab[(t + 3) & 3]);
+        if (t + 4 < ntiles && wave == (t & (NW - 1))) fill_tab(sTab[t & 3], k0 + (t + 4) * TK);
+      }
+    };
+    auto end_interval = [&](int i) __attribute__((always_inline)) {
+      if (!(i & 1)) {
+        const int j = (i >> 1) + 1;
+        if (j < ntiles) {
+          if (j + 1 < ntiles)
+            wait_vmem_n<CPW>();
+          else
+            wait_vmem();
+        }
+      }
+      barrier_lds();
+    };
+    f32x16 st[C::KB];
+    u32x4 pp[TK / 16];
+    if (wave_live) qk(kslot(0), st);
+    if (grp == 0) {
+      if (wave_live) smax(st, k0, nullptr, pp);
+      end_interval(0);
+      for (int t = 0; t < ntiles; ++t) {
+        start_interval(2 * t + 1);
+        if (wave_live) {
+          __builtin_amdgcn_s_setprio(1);
+          pv(vslot(t), pp);
+          if (t + 1 < ntiles) {
+            __builtin_amdgcn_sched_barrier(0);
+            qk(kslot(t + 1), st);
+          }
+          __builtin_amdgcn_s_setprio(0);
+        }
+        end_interval(2 * t + 1);
+        if (t + 1 < ntiles) {
+          start_interval(2 * t + 2);
+          if (wave_live) smax(st, k0 + (t + 1) * TK, nullptr, pp);
+          end_interval(2 * t + 2);
+        }
+      }
+    } else {
+      end_interval(0);
+      for (int t = 0; t < ntiles; ++t) {
+        start_interval(2 * t + 1);
+        if (wave_live) smax(st, k0 + t * TK, nullptr, pp);
+        end_interval(2 * t + 1);
+        start_interval(2 * t + 2);
+        if (wave_live) {
+          __builtin_amdgcn_s_setprio(1);
+          pv(vslot(t), pp);
+          if (t + 1 < ntiles) {
+            __builtin_amdgcn_sched_barrier(0);
+            qk(kslot(t + 1), st);
+          }
+          __builtin_amdgcn_s_setprio(0);
+        }
+        if (t + 1 < ntiles) end_interval(2 * t + 2);
+      }
+    }
+  } else {
+    for (int t = 0; t < ntiles; t += NBUF) {
+      step(I0{}, t);
+      if (t + 1 < ntiles) step(I1{}, t + 1);
+      if constexpr (NBUF > 2) {
+        if (t + 2 < ntiles) step(I2{}, t + 2);
+        if (t + 3 < ntiles) step(I3{}, t + 3);
+      }
     }
   }
 
@@ -840,8 +935,9 @@ __global__ __launch_bounds__(64 * NW, (large_min_groups<D, NW>())) void large_ke
 
 template <int QT, bool FP8, int D, bool FNUZ, bool TS>
 hipError_t launch_large_t(const Params& p, bool split, bool eight, dim3 grid, hipStream_t stream) {
-  if constexpr (D <= 128) {
+  if constexpr (D <= 128 && !FP8) {
     if (eight) {
+      if (p.softcap_on || p.alibi != nullptr || p.qq_bias != nullptr) return hipErrorInvalidValue;
       if (split)
         hipLaunchKernelGGL((large_kernel<QT, FP8, D, true, FNUZ, TS, 8>), grid, dim3(512), 0,
                            stream, p);

@@ -253,6 +253,23 @@ def test_deep_copy_ring_tile_counts():
         assert plan.kernel == 2
 
 
+def test_eight_wave_interval_schedule_tile_counts():
+    """256-row blocks run their two wave halves half a tile apart (two barriers
+    per tile, copies two tiles ahead): partitions of 1 .. 9 tiles, blocks whose
+    last waves hold no rows, sinks, and a window that starts mid-tile."""
+    case = make_case(seqs=[(300, 4400), (40, 4200), (0, 100), (257, 4097)], seed=130,
+                     sinks=True, **BASE)
+    for n_part in (1, 9, 13, 18, 23, 30, 45):
+        path = "2d" if n_part == 1 else "splitkv"
+        _, plan = _check(case, path, n_part, label=f"pp-p{n_part}")
+        assert plan.kernel == 2
+    case = make_case(seqs=[(300, 6000), (33, 5000)], seed=131, window=4100, **BASE)
+    for n_part in (1, 3):
+        path = "2d" if n_part == 1 else "splitkv"
+        _, plan = _check(case, path, n_part, label=f"pp-w-p{n_part}")
+        assert plan.kernel == 2
+
+
 @pytest.mark.parametrize("Hq,Hkv", [(24, 1), (32, 1), (64, 2)])
 def test_wide_group_decode_head_groups(Hq, Hkv):
     """Decode with G > 16 runs as head groups of <= 16 rows on the small kernel;
