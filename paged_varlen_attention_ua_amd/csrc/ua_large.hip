@@ -196,8 +196,9 @@ __global__ __launch_bounds__(64 * NW, (large_min_groups<D, NW>())) void large_ke
   // tiles before it is used; otherwise two deep (measured on MI355X: four deep
   // is 2-4% faster for eight-wave groups and 7% slower for D = 256).
   constexpr int NBUF = (!FP8 && NW == 8) ? 4 : 2;
-  constexpr bool kLazyMax = NW == 8;
-  constexpr bool kPingPong = NW == 8 && !FP8;
+  // Eight-wave groups exist for 16-bit caches only (their launcher).
+  constexpr bool kPingPong = NW == 8;
+  static_assert(NW == 4 || !FP8, "eight-wave groups read 16-bit caches");
   // Ring buffers: K of slot b at sRing + b * TILEB, V at sRing + (NBUF + b) * TILEB.
   __shared__ __attribute__((aligned(1024))) char sRing[2 * NBUF * C::TILEB];
   char* const sK0 = sRing;
@@ -441,55 +442,162 @@ __global__ __launch_bounds__(64 * NW, (large_min_groups<D, NW>())) void large_ke
 
   const int ntiles = (k1 - k0 + TK - 1) / TK;
 
-  // ---- S^T = K Q^T of the tile in LDS buffer sk.
+  // Eight-wave groups (16-bit caches, plain logits: no softcap, ALiBi,
+  // QQ-bias or per-token scales) run the tile in three parts that the two wave
+  // halves interleave (see the interval schedule below): qk, smax, pv.
+  // ---- S^T = K Q^T of the tile in LDS buffer sk.  The scheduling-group hint
+  // used by four-wave groups is not honoured here (the reads landed right
+  // before their MFMAs), so the order is pinned: K reads run four MFMAs ahead.
   auto qk = [&](const char* sk, f32x16* sacc) __attribute__((always_inline)) {
-    if constexpr (NW == 8) {
-      // Eight-wave groups: the scheduling-group hint below is not honoured
-      // here (the reads landed right before their MFMAs), so the order is
-      // pinned: K reads run four MFMAs ahead.
-      constexpr int NQ = C::KB * C::QC;
-      constexpr int LEAD = 4;
-      u32x4 kr[NQ];
+    constexpr int NQ = C::KB * C::QC;
+    constexpr int LEAD = 4;
+    u32x4 kr[NQ];
 #pragma unroll
-      for (int i = 0; i < LEAD; ++i)
-        kr[i] = *reinterpret_cast<const u32x4*>(sk + 32 * (i / C::QC) * ROWB + kaddr[i % C::QC]);
+    for (int i = 0; i < LEAD; ++i)
+      kr[i] = *reinterpret_cast<const u32x4*>(sk + 32 * (i / C::QC) * ROWB + kaddr[i % C::QC]);
 #pragma unroll
-      for (int i = 0; i < NQ; ++i) {
-        if (i + LEAD < NQ) {
-          const int j = i + LEAD;
-          kr[j] = *reinterpret_cast<const u32x4*>(sk + 32 * (j / C::QC) * ROWB + kaddr[j % C::QC]);
-        }
-        const int kb = i / C::QC, c = i % C::QC;
-        sacc[kb] = mfma32<QT>(kr[i], qop[c], c == 0 ? f32x16{} : sacc[kb]);
-        __builtin_amdgcn_sched_barrier(0);
+    for (int i = 0; i < NQ; ++i) {
+      if (i + LEAD < NQ) {
+        const int j = i + LEAD;
+        kr[j] = *reinterpret_cast<const u32x4*>(sk + 32 * (j / C::QC) * ROWB + kaddr[j % C::QC]);
       }
-    } else {
-#pragma unroll
-      for (int kb = 0; kb < C::KB; ++kb) {
-        sacc[kb] = f32x16{};
-#pragma unroll
-        for (int c = 0; c < C::QC; ++c) {
-          const u32x4 a = *reinterpret_cast<const u32x4*>(sk + 32 * kb * ROWB + kaddr[c]);
-          sacc[kb] = mfma32<QT>(a, qop[c], sacc[kb]);
-        }
-      }
-      // Schedule: keep four K reads in flight ahead of the QK MFMAs (the
-      // default schedule issued them two MFMAs ahead, exposing LDS latency;
-      // measured on MI355X: 9% faster for D = 256).
-      __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);  // DS reads
-#pragma unroll
-      for (int k = 0; k < C::KB * C::QC - 4; ++k) {
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
-        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-      }
-      __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
+      const int kb = i / C::QC, c = i % C::QC;
+      sacc[kb] = mfma32<QT>(kr[i], qop[c], c == 0 ? f32x16{} : sacc[kb]);
+      __builtin_amdgcn_sched_barrier(0);
     }
   };
-  // ---- Logits, masks and P of the tile starting at key kt (S^T in sacc):
-  // moves the running maximum and sum (rescaling O when the maximum moves) and
-  // leaves P^T in pop as the B operands of the PV MFMAs.
-  auto smax = [&](f32x16* sacc, int kt, const float* sc, u32x4* pop)
+  // ---- Masks and P of the tile starting at key kt (raw S^T in sacc): moves
+  // the running maximum and sum (rescaling O when the maximum moves) and leaves
+  // P^T in pop as the B operands of the PV MFMAs.  P = 2^(s * c2 - m) is formed
+  // against the running maximum m first; the tile's own maximum is only needed
+  // when m must move, i.e. when some p of the tile exceeds 2^8 (then the sum of
+  // the lane's p exceeds 2^8 too) or the row has no maximum yet and sees keys
+  // of this tile (its p were formed against 0 and may all have underflowed);
+  // when no lane of the wave sees either, the rule "move m when the tile's
+  // maximum exceeds it by more than 8" would not move it (up to the rounding
+  // of exp2), so the tile maximum is skipped.
+  auto smax = [&](f32x16* sacc, int kt, u32x4* pop) __attribute__((always_inline)) {
+    const bool full = kt >= kl && kt + TK <= k1 && kt + TK - 1 <= wave_pmin &&
+                      (p.window <= 0 || kt > wave_pmax - p.window);
+    // key of register r of block kb: kt + 32 kb + 8 (r / 4) + 4 g2 + r % 4;
+    // visible iff row_lo <= key < row_hi, tested as one unsigned compare.
+    if (!full) {
+      const uint32_t span = (uint32_t)max(row_hi - row_lo, 0);
+      const int kd0 = kt + 4 * g2 - row_lo;
+#pragma unroll
+      for (int kb = 0; kb < C::KB; ++kb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int o = 32 * kb + 8 * (r >> 2) + (r & 3);
+          sacc[kb][r] = (uint32_t)(kd0 + o) < span ? sacc[kb][r] : -INFINITY;
+        }
+    }
+    float psum;
+    auto make_p = [&]() __attribute__((always_inline)) {
+      const float m_use = (m_run == -INFINITY) ? 0.0f : m_run;
+      float ps = 0.0f;
+#pragma unroll
+      for (int kk = 0; kk < TK / 16; ++kk) {
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const float a =
+              fast_exp2(__builtin_fmaf(sacc[kk >> 1][8 * (kk & 1) + 2 * q], c2, -m_use));
+          const float b =
+              fast_exp2(__builtin_fmaf(sacc[kk >> 1][8 * (kk & 1) + 2 * q + 1], c2, -m_use));
+          ps += a + b;  // the row sum is of the fp32 p
+          pop[kk][q] = pack2<QT>(a, b);
+        }
+      }
+      psum = ps;
+    };
+    // Tile maximum (across the lane pair (l, l ^ 32) holding the same row, in
+    // base-2 logit units: c2 > 0, and -inf stays -inf); m moves to it when it
+    // exceeds m by more than 8.  Returns whether any row of the wave moved.
+    auto move_max = [&]() __attribute__((always_inline)) -> bool {
+      float mt = -INFINITY;
+#pragma unroll
+      for (int kb = 0; kb < C::KB; ++kb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) mt = fmaxf(mt, sacc[kb][r]);
+      mt = wave_max_xor(mt, 32) * c2;
+      const bool need = mt > m_run + 8.0f;
+      if (!__builtin_amdgcn_ballot_w64(need)) return false;
+      const float m_new = need ? mt : m_run;
+      const float alpha = need ? fast_exp2(m_run - m_new) : 1.0f;  // m_run = -inf -> 0
+      l_run *= alpha;
+#pragma unroll
+      for (int d = 0; d < C::DB; ++d) oacc[d] *= alpha;
+      m_run = m_new;
+      return true;
+    };
+    make_p();
+    const bool first = m_run == -INFINITY && max(kt, row_lo) < min(kt + TK, row_hi);
+    if (__builtin_amdgcn_ballot_w64(!(psum <= 256.0f) || first))
+      if (move_max()) make_p();
+    l_run += psum;
+  };
+  // ---- O^T += V^T P^T (V tile in LDS buffer sv).
+  auto pv = [&](const char* sv, const u32x4* pop) __attribute__((always_inline)) {
+    // With a ring of more than 64 KB the V buffers lie beyond the reads'
+    // 16-bit immediate offset: then the buffer base goes into the address
+    // register with one add per read address and tile (the compiler's own
+    // form took one per read), and only 16 kk rows stay immediate.
+    constexpr bool kVHigh = 2 * NBUF * C::TILEB > 65536;
+    uint32_t vb[2][C::DB];
+    if constexpr (kVHigh) {
+#pragma unroll
+      for (int hh = 0; hh < 2; ++hh)
+#pragma unroll
+        for (int d = 0; d < C::DB; ++d) vb[hh][d] = lds_offset_add(sv, vaddr[hh][d]);
+    }
+#pragma unroll
+    for (int d = 0; d < C::DB; ++d) {
+#pragma unroll
+      for (int kk = 0; kk < TK / 16; ++kk) {
+        u32x2 lo2, hi2;
+        if constexpr (kVHigh) {
+          lo2 = lds_read_tr16_at(vb[0][d] + 16 * kk * ROWB);
+          hi2 = lds_read_tr16_at(vb[1][d] + 16 * kk * ROWB);
+        } else {
+          lo2 = lds_read_tr16(sv + 16 * kk * ROWB + vaddr[0][d]);
+          hi2 = lds_read_tr16(sv + 16 * kk * ROWB + vaddr[1][d]);
+        }
+        oacc[d] = mfma32<QT>(u32x4{lo2[0], lo2[1], hi2[0], hi2[1]}, pop[kk], oacc[d]);
+      }
+    }
+    // Schedule: eight transposed V reads (four MFMAs' operands) in flight ahead
+    // of the PV MFMAs (measured: a further 4% for D = 256).
+    __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);
+#pragma unroll
+    for (int k = 0; k < C::DB * (TK / 16) - 4; ++k) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+    }
+    __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
+  };
+  auto compute = [&](const char* sk, const char* sv, int kt, const float* sc)
       __attribute__((always_inline)) {
+    // ---- S^T = K Q^T
+    f32x16 sacc[C::KB];
+#pragma unroll
+    for (int kb = 0; kb < C::KB; ++kb) {
+      sacc[kb] = f32x16{};
+#pragma unroll
+      for (int c = 0; c < C::QC; ++c) {
+        const u32x4 a = *reinterpret_cast<const u32x4*>(sk + 32 * kb * ROWB + kaddr[c]);
+        sacc[kb] = mfma32<QT>(a, qop[c], sacc[kb]);
+      }
+    }
+    // Schedule: keep four K reads in flight ahead of the QK MFMAs (the
+    // default schedule issued them two MFMAs ahead, exposing LDS latency;
+    // measured on MI355X: 9% faster for D = 256).
+    __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);  // DS reads
+#pragma unroll
+    for (int k = 0; k < C::KB * C::QC - 4; ++k) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+    }
+    __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
     // Per-token K scales: registers 4j .. 4j + 3 of block kb are keys
     // 32 kb + 8 j + 4 g2 + 0..3 of the tile.
     if constexpr (tsc) {
@@ -563,77 +671,16 @@ __global__ __launch_bounds__(64 * NW, (large_min_groups<D, NW>())) void large_ke
           sacc[kb][r] = (uint32_t)(kd0 + o) < span ? sacc[kb][r] : -INFINITY;
         }
     }
-    // ---- P = 2^(s * cs - m), packed as the B operands of the PV MFMAs.
-    // Eight-wave blocks (kLazyMax) form P against the running maximum m
-    // first; the tile's own maximum is only needed
-    // when m must move, i.e. when some p of the tile exceeds 2^8 (then the sum
-    // of the lane's p exceeds 2^8 too) or the row has no maximum yet and sees
-    // keys of this tile (its p were formed against 0 and may all have
-    // underflowed); when no lane of the wave sees either, the rule "move m
-    // when the tile's maximum exceeds it by more than 8" would not move it
-    // (up to the rounding of exp2), so the tile maximum is skipped.  This
-    // puts a branch between the exp2s and the PV MFMAs, which a second wave
-    // on the SIMD covers: measured on MI355X, 2-4% faster with eight waves
-    // (head dim <= 128) and 5-11% slower with four (head dim 64 and 256).
+    // ---- P = 2^(s * cs - m), packed as the B operands of the PV MFMAs; the
+    // running maximum moves first when the tile's maximum exceeds it by more
+    // than 8.
+    u32x4 pop[TK / 16];
     float psum;
-    auto make_p = [&]() __attribute__((always_inline)) {
-      const float m_use = (m_run == -INFINITY) ? 0.0f : m_run;
-      float ps = 0.0f;
-#pragma unroll
-      for (int kk = 0; kk < TK / 16; ++kk) {
-        // V scales of this operand's keys 16 kk + 4 g2 + {0..3, 8..11} (q = 0..3).
-        f32x4 v4[2] = {f32x4{1.f, 1.f, 1.f, 1.f}, f32x4{1.f, 1.f, 1.f, 1.f}};
-        if constexpr (tsc) {
-          v4[0] = *reinterpret_cast<const f32x4*>(sc + TK + 16 * kk + 4 * g2);
-          v4[1] = *reinterpret_cast<const f32x4*>(sc + TK + 16 * kk + 4 * g2 + 8);
-        }
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const float a =
-              fast_exp2(__builtin_fmaf(sacc[kk >> 1][8 * (kk & 1) + 2 * q], cs, -m_use));
-          const float b =
-              fast_exp2(__builtin_fmaf(sacc[kk >> 1][8 * (kk & 1) + 2 * q + 1], cs, -m_use));
-          // The row sum is of the fp32 p (per-token V scales excluded).  One
-          // accumulator: head dim 256 runs at the register limit, where a
-          // second one cost the K reads their lead over the QK MFMAs.
-          ps += a + b;
-          if constexpr (tsc)
-            pop[kk][q] = pack2<QT>(a * v4[q >> 1][2 * (q & 1)], b * v4[q >> 1][2 * (q & 1) + 1]);
-          else
-            pop[kk][q] = pack2<QT>(a, b);
-        }
-      }
-      psum = ps;
-    };
-    // Tile maximum (across the lane pair (l, l ^ 32) holding the same row, in
-    // base-2 logit units: cs > 0, and -inf stays -inf); m moves to it when it
-    // exceeds m by more than 8.  Returns whether any row of the wave moved.
-    auto move_max = [&]() __attribute__((always_inline)) -> bool {
-      float mt = -INFINITY;
-#pragma unroll
-      for (int kb = 0; kb < C::KB; ++kb)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) mt = fmaxf(mt, sacc[kb][r]);
-      mt = wave_max_xor(mt, 32) * cs;
-      const bool need = mt > m_run + 8.0f;
-      if (!__builtin_amdgcn_ballot_w64(need)) return false;
-      const float m_new = need ? mt : m_run;
-      const float alpha = need ? fast_exp2(m_run - m_new) : 1.0f;  // m_run = -inf -> 0
-      l_run *= alpha;
-#pragma unroll
-      for (int d = 0; d < C::DB; ++d) oacc[d] *= alpha;
-      m_run = m_new;
-      return true;
-    };
-    if constexpr (kLazyMax) {
-      make_p();
-      const bool first = m_run == -INFINITY && max(kt, row_lo) < min(kt + TK, row_hi);
-      if (__builtin_amdgcn_ballot_w64(!(psum <= 256.0f) || first))
-        if (move_max()) make_p();
-    } else {
-      // Written out rather than through the lambdas: head dim 256 runs at the
-      // register limit, and the lambda form cost the K reads their lead over
-      // the QK MFMAs there.
+    {
+      // Four-wave groups keep QK, softmax and PV in one body: head dim 256
+      // runs at the register limit, where composing it from the eight-wave
+      // parts (or from lambdas) cost the K reads their lead over the QK MFMAs
+      // (measured on MI355X: 17% slower).
       float mt = -INFINITY;
 #pragma unroll
       for (int kb = 0; kb < C::KB; ++kb)
@@ -673,9 +720,7 @@ __global__ __launch_bounds__(64 * NW, (large_min_groups<D, NW>())) void large_ke
       }
     }
     l_run += psum;
-  };
-  // ---- O^T += V^T P^T (V tile in LDS buffer sv).
-  auto pv = [&](const char* sv, const u32x4* pop) __attribute__((always_inline)) {
+    // ---- O^T += V^T P^T
     // With a ring of more than 64 KB the V buffers lie beyond the reads'
     // 16-bit immediate offset: then the buffer base goes into the address
     // register with one add per read address and tile (the compiler's own
@@ -712,14 +757,6 @@ __global__ __launch_bounds__(64 * NW, (large_min_groups<D, NW>())) void large_ke
       __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
     }
     __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
-  };
-  auto compute = [&](const char* sk, const char* sv, int kt, const float* sc)
-      __attribute__((always_inline)) {
-    f32x16 sacc[C::KB];
-    u32x4 pop[TK / 16];
-    qk(sk, sacc);
-    smax(sacc, kt, sc, pop);
-    pv(sv, pop);
   };
 
   // Buffer B of the ring (compile-time B).
@@ -842,7 +879,7 @@ __global__ __launch_bounds__(64 * NW, (large_min_groups<D, NW>())) void large_ke
     u32x4 pp[TK / 16];
     if (wave_live) qk(kslot(0), st);
     if (grp == 0) {
-      if (wave_live) smax(st, k0, nullptr, pp);
+      if (wave_live) smax(st, k0, pp);
       end_interval(0);
       for (int t = 0; t < ntiles; ++t) {
         start_interval(2 * t + 1);
@@ -858,7 +895,7 @@ __global__ __launch_bounds__(64 * NW, (large_min_groups<D, NW>())) void large_ke
         end_interval(2 * t + 1);
         if (t + 1 < ntiles) {
           start_interval(2 * t + 2);
-          if (wave_live) smax(st, k0 + (t + 1) * TK, nullptr, pp);
+          if (wave_live) smax(st, k0 + (t + 1) * TK, pp);
           end_interval(2 * t + 2);
         }
       }
@@ -866,7 +903,7 @@ __global__ __launch_bounds__(64 * NW, (large_min_groups<D, NW>())) void large_ke
       end_interval(0);
       for (int t = 0; t < ntiles; ++t) {
         start_interval(2 * t + 1);
-        if (wave_live) smax(st, k0 + t * TK, nullptr, pp);
+        if (wave_live) smax(st, k0 + t * TK, pp);
         end_interval(2 * t + 1);
         start_interval(2 * t + 2);
         if (wave_live) {
