@@ -271,15 +271,18 @@ ua_status ua_plan(const ua_problem* prob, int32_t num_cus, int32_t force_path,
   if (prob->window > 0) eff_k = std::min<int64_t>(eff_k, (int64_t)prob->window + bq - 1);
   const int64_t wgs = est_blocks * prob->num_kv_heads * HG;
 
-  // Automatic partition count: fill about four small workgroups per CU,
-  // keep at least 256 keys per partition, and stay one-pass for short ranges.
+  // Automatic partition count: fill the device with small workgroups, keep at
+  // least two tiles per partition, and stay one-pass for short ranges.
   int auto_parts = 1;
   if (small && wgs > 0 && wgs < num_cus && eff_k > 1024) {
     // Measured on MI355X: about one small workgroup per CU for 16-bit KV and two
-    // for fp8 KV (half the bytes per key), at least 256 keys per partition.
+    // for fp8 KV (half the bytes per key).  At least 64 keys per partition:
+    // decode of a few sequences is latency-bound, and 32 partitions of its
+    // 4096-key or 2048-key (d256) ranges ran 7% and 24% faster than the 16 and
+    // 8 that a 256-key minimum gave.
     const int64_t per_cu = is_fp8(prob->kv_dtype) ? 2 : 1;
     const int64_t want = ceil_div(per_cu * num_cus, wgs);
-    const int64_t by_len = std::max<int64_t>(1, eff_k / 256);
+    const int64_t by_len = std::max<int64_t>(1, eff_k / 64);
     auto_parts = (int)std::max<int64_t>(1, std::min<int64_t>(std::min(want, by_len), 64));
   } else if (!small && wgs > 0 && wgs < (eight ? 1ll : 2ll) * num_cus && eff_k >= 1024) {
     // Four-wave large blocks run two per CU, eight-wave ones one: split a grid

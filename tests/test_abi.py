@@ -82,6 +82,17 @@ def test_long_decode_splits_to_fill_the_device():
     assert st == 0 and plan.n_part == 8
 
 
+def test_few_sequence_decode_splits_to_two_tile_partitions():
+    # 4 sequences x 2 kv heads (fp16 decode, longest 4096 keys): 256 / 8 = 32
+    # partitions of 128 keys; 2 sequences of d256 (longest 2048): 2048 / 64 = 32.
+    f16 = dict(q_dtype=B.UA_F16, kv_dtype=B.UA_F16, o_dtype=B.UA_F16, window=0,
+               num_q_heads=16, num_kv_heads=2)
+    st, plan = status_of(problem(num_seqs=4, total_q=4, max_seqlen_k=4096, **f16))
+    assert st == 0 and plan.path == B.UA_PATH_SPLITKV and plan.n_part == 32
+    st, plan = status_of(problem(num_seqs=2, total_q=2, max_seqlen_k=2048, head_dim=256, **f16))
+    assert st == 0 and plan.path == B.UA_PATH_SPLITKV and plan.n_part == 32
+
+
 def test_short_context_full_grid_stays_one_pass():
     st, plan = status_of(problem(num_seqs=32, total_q=32, max_seqlen_k=630))
     assert st == 0 and plan.path == B.UA_PATH_2D and plan.n_part == 1
