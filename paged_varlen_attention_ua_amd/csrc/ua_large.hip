@@ -4,8 +4,9 @@
 // block_q = 32 NW / G tokens times the G query heads of the kv head (grouped
 // rows share every K/V tile).  NW = 4 or 8 waves own 32 rows each; every K/V
 // tile staged in LDS serves all of them, so 8 waves halve the K/V reads per
-// flop (they come from L2 and bound long chunks).  Per 64-key tile (32 keys for
-// head dim 256):
+// flop (they come from L2 and bound long chunks); their two halves of four
+// waves run half a tile apart, one half's MFMAs between two barriers while the
+// other half runs its softmax.  Per 64-key tile (32 keys for head dim 256):
 //   * the byte offsets of the tile's K/V rows are looked up through the block
 //     table one tile ahead (its entries for the workgroup's key range are
 //     staged in LDS once) by one wave, into a small LDS table;
@@ -191,17 +192,18 @@ __global__ __launch_bounds__(64 * NW, (large_min_groups<D, NW>())) void large_ke
   using C = LargeCfg<D, NW>;
   constexpr int TK = C::TK;
   constexpr int ROWB = C::ROWB;
-  // K/V tile ring: NBUF buffers each.  16-bit caches in eight-wave groups
-  // (one per CU, LDS to spare) run four deep, so a tile's copy is issued three
-  // tiles before it is used; otherwise two deep (measured on MI355X: four deep
-  // is 2-4% faster for eight-wave groups and 7% slower for D = 256).
-  constexpr int NBUF = (!FP8 && NW == 8) ? 4 : 2;
-  // Eight-wave groups exist for 16-bit caches only (their launcher).
+  // Eight-wave groups exist for 16-bit caches only (their launcher) and run
+  // the two-half interval schedule.
   constexpr bool kPingPong = NW == 8;
   static_assert(NW == 4 || !FP8, "eight-wave groups read 16-bit caches");
+  // K/V tile ring: NBUF buffers each.  Eight-wave groups (one per CU, LDS to
+  // spare) run four deep, with each tile's copy issued two tiles (four
+  // intervals) before it is first read; four-wave groups two deep, the copy of
+  // tile t + 1 in flight while tile t is computed (measured on MI355X: a
+  // four-deep ring was 7% slower for D = 256).
+  constexpr int NBUF = NW == 8 ? 4 : 2;
   // Ring buffers: K of slot b at sRing + b * TILEB, V at sRing + (NBUF + b) * TILEB.
   __shared__ __attribute__((aligned(1024))) char sRing[2 * NBUF * C::TILEB];
-  char* const sK0 = sRing;
   // Row-offset table of tile t in slot t % NBUF.
   __shared__ int64_t sTab[NBUF][TK];
   __shared__ int32_t sm_pg[C::MAXPG];
