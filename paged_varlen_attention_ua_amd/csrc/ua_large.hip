@@ -836,8 +836,11 @@ __global__ __launch_bounds__(64 * NW, (large_min_groups<D, NW>())) void large_ke
     // 4-7 (B), one of each on every SIMD, half a tile apart: between two
     // barriers one half runs MFMAs (PV of tile t, then QK of tile t + 1)
     // while the other runs the softmax VALU work of its tile, and the next
-    // interval they swap, so each SIMD's matrix and vector pipes work at the
-    // same time instead of both waves taking turns on one of them.
+    // interval they swap, so one wave's MFMAs run beside the other wave's VALU
+    // work (the MFMA half at raised wave priority).  Measured on MI355X: 0-3%
+    // faster than both halves in step; one wave alone issues VALU work at half
+    // the SIMD's rate, and MFMAs slow the other wave's VALU stream, which
+    // bound the gain.
     //   interval 0:        A: QK(0), softmax(0)       B: QK(0)
     //   interval 2t + 1:   A: PV(t), QK(t + 1)        B: softmax(t)
     //   interval 2t + 2:   A: softmax(t + 1)          B: PV(t), QK(t + 1)
