@@ -270,6 +270,17 @@ def test_eight_wave_interval_schedule_tile_counts():
         assert plan.kernel == 2
 
 
+@pytest.mark.parametrize("D,dt", [(64, "bf16"), (128, "f16"), (64, "f16")])
+def test_eight_wave_head_dims_and_dtypes(D, dt):
+    """The 256-row (eight-wave) kernel for the other head dim and query dtype it
+    is built for: one pass and split, with sinks and a short second sequence."""
+    case = make_case(seqs=[(40, 4300), (3, 800)], seed=140 + D, sinks=True,
+                     **dict(BASE, head_dim=D, q_dtype=dt))
+    for path, n_part in (("2d", 0), ("splitkv", 3)):
+        _, plan = _check(case, path, n_part, label=f"eight-d{D}-{dt}-{path}")
+        assert plan.kernel == 2
+
+
 @pytest.mark.parametrize("Hq,Hkv", [(24, 1), (32, 1), (64, 2)])
 def test_wide_group_decode_head_groups(Hq, Hkv):
     """Decode with G > 16 runs as head groups of <= 16 rows on the small kernel;
