@@ -286,13 +286,15 @@ ua_status ua_plan(const ua_problem* prob, int32_t num_cus, int32_t force_path,
     auto_parts = (int)std::max<int64_t>(1, std::min<int64_t>(std::min(want, by_len), 64));
   } else if (!small && wgs > 0 && wgs < (eight ? 1ll : 2ll) * num_cus && eff_k >= 1024) {
     // Four-wave large blocks run two per CU, eight-wave ones one: split a grid
-    // that does not fill that, keeping at least 512 keys per partition (256
-    // and up to 64 partitions when at most half of a block's rows are live,
-    // e.g. decode with G > 16: there the key walk is bandwidth-shaped like the
-    // small blocks').
+    // that does not fill that, keeping at least 256 keys (four tiles) per
+    // partition, up to 16 partitions (64 when at most half of a block's rows
+    // are live, e.g. decode with G > 16: there the key walk is bandwidth-shaped
+    // like the small blocks').  Measured on MI355X: the mixed decode + prefill
+    // batch (longest range 1328 keys) ran 20-25% faster at the 5 partitions of
+    // a 256-key minimum than at the 2 of a 512-key one.
     const bool sparse_rows = (int64_t)std::min(prob->max_seqlen_q, bq) * G * 2 <= kLargeRows;
     const int64_t want = ceil_div((eight ? 1ll : 2ll) * num_cus, wgs);
-    const int64_t by_len = std::max<int64_t>(1, eff_k / (sparse_rows ? 256 : 512));
+    const int64_t by_len = std::max<int64_t>(1, eff_k / 256);
     auto_parts = (int)std::max<int64_t>(
         1, std::min<int64_t>(std::min(want, by_len), sparse_rows ? 64 : 16));
   }

@@ -93,6 +93,16 @@ def test_few_sequence_decode_splits_to_two_tile_partitions():
     assert st == 0 and plan.path == B.UA_PATH_SPLITKV and plan.n_part == 32
 
 
+def test_mixed_batch_splits_to_four_tile_partitions():
+    # (q, kv) = (1, 1328), (5, 18), (129, 463), (64, 64), (128, 256), 16q/2kv
+    # fp16: 128-row blocks (16 tokens x G = 8) leave CUs idle; the longest key
+    # range (1328) in partitions of at least 256 keys gives 5.
+    st, plan = status_of(problem(num_seqs=5, total_q=327, max_seqlen_q=129, max_seqlen_k=1328,
+                                 num_q_heads=16, num_kv_heads=2, window=0, q_dtype=B.UA_F16,
+                                 kv_dtype=B.UA_F16, o_dtype=B.UA_F16))
+    assert st == 0 and plan.kernel == 1 and plan.path == B.UA_PATH_SPLITKV and plan.n_part == 5
+
+
 def test_short_context_full_grid_stays_one_pass():
     st, plan = status_of(problem(num_seqs=32, total_q=32, max_seqlen_k=630))
     assert st == 0 and plan.path == B.UA_PATH_2D and plan.n_part == 1
