@@ -103,6 +103,20 @@ def test_mixed_batch_splits_to_four_tile_partitions():
     assert st == 0 and plan.kernel == 1 and plan.path == B.UA_PATH_SPLITKV and plan.n_part == 5
 
 
+def test_eight_wave_blocks_only_for_plain_logits():
+    # A long chunked prefill (2048 queries behind 16384 keys, 32q/8kv, bf16)
+    # takes 256-row blocks; with softcap, ALiBi or a QQ-bias it must take the
+    # 128-row kernel, the one with those paths.
+    long_prefill = dict(num_seqs=1, total_q=2048, max_seqlen_q=2048, max_seqlen_k=18432,
+                        window=0, num_blocks=2400, max_blocks_per_seq=1200)
+    st, plan = status_of(problem(**long_prefill))
+    assert st == 0 and plan.kernel == 2
+    for extra in (dict(softcap=30.0), dict(has_alibi=1),
+                  dict(has_qq_bias=1, qq_bias_stride=2048)):
+        st, plan = status_of(problem(**long_prefill, **extra))
+        assert st == 0 and plan.kernel == 1, extra
+
+
 def test_short_context_full_grid_stays_one_pass():
     st, plan = status_of(problem(num_seqs=32, total_q=32, max_seqlen_k=630))
     assert st == 0 and plan.path == B.UA_PATH_2D and plan.n_part == 1
