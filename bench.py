@@ -13,9 +13,11 @@ Inputs are resident in HBM when timing starts and are rotated over R copies
 R = max(2, ceil(1 GiB / bytes touched per step)).
 
 Also reported on the same line: the other decode workloads (GB/s), the
-chunked-prefill workloads (TFLOP/s of 4 * D * Hq * visible (q, k) pairs), the
-dominant kernel's roofline with HIP-event timing, and the CPU oracle's rate on
-a bounded sample (cpu_baseline).
+chunked-prefill workloads (TFLOP/s of 4 * D * Hq * visible (q, k) pairs, per
+step and kernel-only), the decode kernel's HBM roofline and the prefill
+kernel's MFMA roofline (2k chunk behind a 16k prefix) with HIP-event timing and
+the graphics clock sampled under sustained load, and the CPU oracle's rate on
+bounded samples of both (cpu_baseline, prefill_cpu_baseline).
 """
 
 import argparse
@@ -32,6 +34,12 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
 MFMA_PEAK_TFLOPS = {"f16": 2500.0, "bf16": 2500.0}
+# Dense fp16/bf16 MFMA rate of gfx950: 1024 flop per clock per SIMD (a
+# 32x32x16 MFMA, 32768 flop, issues every 32 cycles), 4 SIMDs per CU, 256 CUs.
+MFMA_FLOP_PER_CLK_PER_CU = 4 * 1024
+NUM_CUS = 256
+PEAK_SCLK_MHZ = 2400.0
+PREFILL_HEADLINE = "prefill_chunk2k_prefix16k_bf16"
 HEADLINE = "long_decode_bf16_d128_32q8kv_w4096"
 METRIC = "decode KV GB/s (% of HBM peak) + prefill TFLOP/s (% MFMA peak), 1 GPU"
 EB = {"f16": 2, "bf16": 2, "e4m3fn": 1, "e4m3fnuz": 1}
@@ -310,11 +318,7 @@ def cpu_baseline(case, budget_s=15.0):
     """The oracle, untouched, on a bounded sample of the headline workload."""
     import numpy as np
     import oracle
-    try:
-        from threadpoolctl import threadpool_info
-        cores = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
-    except Exception:
-        cores = os.cpu_count() or 1
+    cores = blas_threads()
     n = len(case["seq_lens"])
     done_bytes = 0
     t0 = time.perf_counter()
@@ -334,9 +338,163 @@ def cpu_baseline(case, budget_s=15.0):
             break
     dt = time.perf_counter() - t0
     return {"value": round(done_bytes / dt / 1e9, 4), "unit": "GB/s", "cores": int(cores),
-            "kind": "oracle",
+            "cpu_model": cpu_model(), "kind": "oracle",
             "sample": f"float64 numpy oracle over whole sequences of the headline workload, "
-                      f"{done_bytes / 1e6:.1f} MB of algorithmic bytes in {dt:.1f} s"}
+                      f"{done_bytes / 1e6:.1f} MB of algorithmic bytes in {dt:.1f} s; BLAS "
+                      f"calls use the stated threads, elementwise numpy work one"}
+
+
+def cpu_model():
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
+
+
+def blas_threads():
+    try:
+        from threadpoolctl import threadpool_info
+        return max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:
+        return os.cpu_count() or 1
+
+
+class SclkSampler:
+    """Current graphics clock (MHz) read from the driver on a host thread every
+    few milliseconds while the GPU runs a sustained load: amdsmi's GFX clock,
+    else the starred level of sysfs pp_dpm_sclk.  Read-only driver queries."""
+
+    def __init__(self):
+        self.samples, self.source, self._read = [], None, None
+        try:
+            import amdsmi
+            amdsmi.amdsmi_init()
+            h = amdsmi.amdsmi_get_processor_handles()[0]
+            amdsmi.amdsmi_get_clock_info(h, amdsmi.AmdSmiClkType.GFX)
+            self._read = lambda: float(
+                amdsmi.amdsmi_get_clock_info(h, amdsmi.AmdSmiClkType.GFX)["clk"])
+            self.source = "amdsmi GFX clock"
+        except Exception:
+            import glob
+            files = sorted(glob.glob("/sys/class/drm/card*/device/pp_dpm_sclk"))
+            if files:
+                def rd(f=files[0]):
+                    for line in open(f):
+                        if line.strip().endswith("*"):
+                            return float(line.split(":")[1].strip().rstrip("*").strip()
+                                         .lower().replace("mhz", ""))
+                    return None
+                try:
+                    rd()
+                    self._read, self.source = rd, "sysfs pp_dpm_sclk"
+                except Exception:
+                    pass
+
+    def run(self, fn):
+        import threading
+        if self._read is None:
+            fn()
+            return
+        stop = threading.Event()
+
+        def loop():
+            while not stop.is_set():
+                try:
+                    v = self._read()
+                    if v:
+                        self.samples.append(v)
+                except Exception:
+                    pass
+                time.sleep(0.005)
+        th = threading.Thread(target=loop, daemon=True)
+        th.start()
+        try:
+            fn()
+        finally:
+            stop.set()
+            th.join()
+
+    def median(self):
+        if not self.samples:
+            return None
+        v = sorted(self.samples)
+        return v[len(v) // 2]
+
+
+def prefill_roofline(case, steps, warmup, name):
+    """Measured MFMA roofline record of the prefill kernel on one workload:
+    kernel-only time from a HIP-graph replay of the main kernel alone (HIP
+    events on the replay stream), plus the graphics clock sampled while the
+    same kernel runs back to back for about a second."""
+    import torch
+    rr = time_case(case, steps, warmup, touched=decode_bytes(case), kernel_events=True)
+    fl = prefill_flops(case)
+    kt = fl / (rr["kernel_ms"] * 1e-3) / 1e12
+    st = fl / (rr["ms_per_step"] * 1e-3) / 1e12
+    peak = MFMA_PEAK_TFLOPS["bf16"]
+    # Sustained load for the clock reading.
+    from tests.gpu_common import to_device
+    r = Runner(case, to_device(case))
+    sp = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    n = max(8, int(1.0 / max(rr["kernel_ms"] * 1e-3, 1e-5)))
+    sampler = SclkSampler()
+
+    def load():
+        for _ in range(n):
+            r.step_main(sp)
+        torch.cuda.synchronize()
+    load()  # ramp
+    sampler.run(load)
+    mhz = sampler.median()
+    rec = {"workload": name, "bound": "mfma", "kernel": "large_kernel " + KERNEL_NAMES[rr["kernel"]],
+           "path": "splitkv" if rr["path"] == 2 else "2d", "n_part": rr["n_part"],
+           "algorithmic_flop": fl, "kernel_ms": round(rr["kernel_ms"], 5),
+           "achieved": round(kt, 2), "peak": peak, "unit": "TFLOP/s",
+           "frac": round(kt / peak, 4),
+           "step_ms": round(rr["ms_per_step"], 5), "step_tflops": round(st, 2),
+           "peak_derivation": f"{NUM_CUS} CU x {MFMA_FLOP_PER_CLK_PER_CU} flop/clk "
+                              f"(dense bf16 MFMA) x {PEAK_SCLK_MHZ / 1000:.1f} GHz = "
+                              f"{NUM_CUS * MFMA_FLOP_PER_CLK_PER_CU * PEAK_SCLK_MHZ / 1e6:.0f} "
+                              f"TFLOP/s (published figure {peak:.0f})",
+           "sclk_under_load_mhz": mhz, "sclk_source": sampler.source,
+           "sclk_samples": len(sampler.samples)}
+    if mhz:
+        pk = NUM_CUS * MFMA_FLOP_PER_CLK_PER_CU * mhz / 1e6
+        rec["peak_at_sclk"] = round(pk, 1)
+        rec["frac_at_sclk"] = round(kt / pk, 4)
+    return rec
+
+
+def prefill_cpu_baseline(case, budget_s=8.0, chunk=32, seed=5):
+    """The oracle, untouched, on random chunks of query rows of a prefill
+    workload: float64 GFLOP/s of the visible (q, k) pairs it covered."""
+    import numpy as np
+    import oracle
+    rng = np.random.default_rng(seed)
+    total_q = case["q"].shape[0]
+    cu = case["cu_seqlens_q"]
+    Hq, D, W = case["num_q_heads"], case["head_dim"], case["window"]
+    flops, rows_done = 0.0, 0
+    t0 = time.perf_counter()
+    while time.perf_counter() - t0 < budget_s:
+        r0 = int(rng.integers(0, max(1, total_q - chunk + 1)))
+        rows = np.arange(r0, min(total_q, r0 + chunk))
+        oracle.attention(**case, rows=rows)
+        for t in rows:
+            s = int(np.searchsorted(cu, t, side="right") - 1)
+            pos = int(case["seq_lens"][s]) - int(cu[s + 1] - cu[s]) + int(t - cu[s])
+            flops += 4.0 * D * Hq * ((pos + 1) if W <= 0 else min(pos + 1, W))
+        rows_done += len(rows)
+    dt = time.perf_counter() - t0
+    return {"value": round(flops / dt / 1e9, 3), "unit": "GFLOP/s", "cores": int(blas_threads()),
+            "cpu_model": cpu_model(), "kind": "oracle",
+            "sample": f"float64 numpy oracle on {rows_done} query rows (random chunks of "
+                      f"{chunk}) of the 2k-chunk-behind-16k-prefix prefill, "
+                      f"{flops / 1e9:.1f} GFLOP of visible pairs in {dt:.1f} s; BLAS calls "
+                      f"use the stated threads, elementwise numpy work one"}
 
 
 def main():
@@ -414,6 +572,11 @@ def main():
         "roofline": {"bound": "hbm", "achieved": round(k_gbs, 2), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(k_gbs / HBM_PEAK_GBS, 4),
                      "traffic": traffic,
+                     "traffic_source": ("stored: rocprofv3 FETCH_SIZE + WRITE_SIZE of this "
+                                        "kernel, calibrated by a 256 MiB copy, in "
+                                        "profiles/counters_split_kernel_long_decode.json; "
+                                        f"valid for kernel source digest {kernel_source_digest()}")
+                     if traffic is not None else "counters not taken on these sources",
                      "kernel": "small_kernel (split-KV partitions)" if r["path"] == 2
                      else "small_kernel (one pass)",
                      "kernel_ms": round(r["kernel_ms"], 5)},
@@ -447,15 +610,22 @@ def main():
             c = make_case(**WORKLOADS[name], poison=False)
             fl = prefill_flops(c)
             rr = time_case(c, max(5, args.steps // 5), 3, touched=decode_bytes(c),
-                           kernel_events=False)
+                           kernel_events=True)
             tf = fl / (rr["ms_per_step"] * 1e-3) / 1e12
+            ktf = fl / (rr["kernel_ms"] * 1e-3) / 1e12
             pre[name] = {"TFLOP/s": round(tf, 2),
                          "exp2_per_call": visible_pairs(c) * c["num_q_heads"],
                          "pct_mfma_peak": round(100 * tf / MFMA_PEAK_TFLOPS["bf16"], 2),
                          "ms_per_step": round(rr["ms_per_step"], 4),
+                         "kernel_ms": round(rr["kernel_ms"], 4),
+                         "kernel_TFLOP/s": round(ktf, 2),
                          "path": "splitkv" if rr["path"] == 2 else "2d",
+                         "n_part": rr["n_part"],
                          "kernel": KERNEL_NAMES[rr["kernel"]]}
         line["prefill"] = pre
+        c = make_case(**WORKLOADS[PREFILL_HEADLINE], poison=False)
+        line["prefill_roofline"] = prefill_roofline(c, max(5, args.steps // 5), 3,
+                                                    PREFILL_HEADLINE)
         lat = {}
         for name in ["mixed_fp16_d128_16q2kv", "mixed_fp16_d128_16q2kv_alibi",
                      "qq_bias_prefill_fp16_d128_16q2kv"]:
@@ -468,6 +638,9 @@ def main():
         line["latency_bound"] = lat
     if not args.no_cpu:
         line["cpu_baseline"] = cpu_baseline(make_case(**WORKLOADS[HEADLINE]))
+        if not args.quick:
+            line["prefill_cpu_baseline"] = prefill_cpu_baseline(
+                make_case(**WORKLOADS[PREFILL_HEADLINE]))
     print(json.dumps(line), flush=True)
 
 

@@ -150,7 +150,12 @@ typedef struct {
   void* out;                   /* [total_q, Hq, D] o_dtype */
   float* lse;                  /* optional [total_q, Hq] fp32 log-sum-exp (natural log,
                                   sink included; -inf for a row that sees nothing
-                                  and has no sink), or NULL */
+                                  and has no sink), or NULL.  It is the log of the
+                                  normaliser the output was divided by; the weights
+                                  enter the P*V product rounded to q_dtype (small
+                                  query blocks sum them as rounded), so it is within
+                                  ln(1 + 2^-8) (bf16) or ln(1 + 2^-11) (fp16) of
+                                  the exact value. */
   const float* qq_bias;        /* [>= max_seqlen_q, qq_bias_stride] fp32 or NULL
                                   (must match has_qq_bias) */
   const float* k_token_scales; /* per-token K scales or NULL (must match
@@ -181,11 +186,16 @@ ua_status ua_forward_2d(const ua_problem* prob, const ua_plan_t* plan, const ua_
  * Split-KV partition pass; requires plan->path == UA_PATH_SPLITKV and a
  * workspace of at least plan->workspace_bytes (256-byte aligned).  Writes,
  * for every query row r (token, head) and partition p, fp32 values
- *   m[p][r]   max base-2 logit (x * log2 e) over the partition's visible keys,
- *   l[p][r]   sum of 2^(x*log2e - m) over those keys (0: partition saw nothing),
- *   acc[p][r][D]  sum of 2^(x*log2e - m) * v (v without v_scale),
- * at workspace offsets 0, P*R*4 and ua_workspace_acc_offset(), R = total_q*Hq.
- * Entries with l == 0 leave m and acc unspecified.  Does not write args->out.
+ *   m[p][r]   the base-2 reference the partition's weights are taken against:
+ *             within 8 of the largest base-2 logit (x * log2 e) over the
+ *             partition's visible keys (small query blocks, plan->kernel 0:
+ *             that largest logit rounded up to an integer),
+ *   l[p][r]   sum of the weights w = 2^(x*log2e - m) over those keys (0: the
+ *             partition saw nothing),
+ *   acc[p][r][D]  sum of w * v (v without v_scale),
+ * at workspace offsets 0, P*R*4 and ua_workspace_acc_offset(), P = n_part,
+ * R = total_q*Hq.  Entries with l == 0 leave m and acc unspecified.  Does not
+ * write args->out.
  */
 ua_status ua_forward_splitkv(const ua_problem* prob, const ua_plan_t* plan, const ua_args* args,
                              void* workspace, size_t workspace_bytes, void* stream);
@@ -194,7 +204,8 @@ ua_status ua_forward_splitkv(const ua_problem* prob, const ua_plan_t* plan, cons
  * Merge the partition states of ua_forward_splitkv into args->out (and
  * args->lse): M = max over partitions with l > 0 (and the sink), L = sum
  * l_p 2^(m_p - M) (+ 2^(sink*log2e - M)), out = v_scale * sum acc_p 2^(m_p - M) / L,
- * zeros when no partition saw a key (AITER PR #3962 review reply).
+ * lse = (M + log2 L) ln 2, zeros when no partition saw a key (AITER PR #3962
+ * review reply).
  */
 ua_status ua_reduce(const ua_problem* prob, const ua_plan_t* plan, const ua_args* args,
                     const void* workspace, size_t workspace_bytes, void* stream);

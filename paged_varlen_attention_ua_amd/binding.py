@@ -81,6 +81,9 @@ def lib():
     global _lib
     with _lib_lock:
         if _lib is None:
+            # torch first: the library must bind to the HIP runtime torch loaded
+            # (a second runtime loaded before torch's sees no device).
+            import torch  # noqa: F401
             if not os.path.exists(LIB_PATH):
                 raise ImportError(
                     f"{LIB_PATH} is missing: build it with "

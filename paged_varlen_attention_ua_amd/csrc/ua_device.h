@@ -57,24 +57,6 @@ __device__ __forceinline__ uint32_t pack2(float a, float b) {
   }
 }
 
-// Low / high 16-bit value of a packed pair back to fp32 (exact).
-template <int QT>
-__device__ __forceinline__ float lo16(uint32_t v) {
-  if constexpr (QT == UA_F16) {
-    return (float)__builtin_bit_cast(f16x2, v)[0];
-  } else {
-    return __builtin_bit_cast(float, v << 16);
-  }
-}
-template <int QT>
-__device__ __forceinline__ float hi16(uint32_t v) {
-  if constexpr (QT == UA_F16) {
-    return (float)__builtin_bit_cast(f16x2, v)[1];
-  } else {
-    return __builtin_bit_cast(float, v & 0xffff0000u);
-  }
-}
-
 // Byte permute: result byte i = byte sel_i of the 8-byte value {hi:lo}.
 __device__ __forceinline__ uint32_t perm_b32(uint32_t hi, uint32_t lo, uint32_t sel) {
   return __builtin_amdgcn_perm(hi, lo, sel);

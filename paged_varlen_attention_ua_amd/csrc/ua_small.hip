@@ -42,6 +42,34 @@
 namespace ua {
 namespace {
 
+// Running maxima of the online softmax (base-2 logit units) are kept at whole
+// numbers: the maximum m a row's p = 2^(x - m) are formed against is rounded
+// up to an integer.  p <= 1 still holds at the row maximum, but the mantissa
+// of p is then 2^frac(x) whatever m is, so the 16-bit rounding of p before
+// the PV MFMA is the same in every partition, wave or tile order, and every
+// rescale factor 2^(m_old - m_new) (and each partition's weight in the merge)
+// is an exact power of two: split and one-pass results differ only by the
+// order of fp32 additions.  -inf stays -inf.
+// The row sum l that normalises O (and gives the log-sum-exp) is the sum of p
+// exactly as rounded for the PV MFMA, so O / l is a convex combination of V
+// rows (exact for a row that sees one key) and O and the log-sum-exp agree
+// with each other; the log-sum-exp then carries the 16-bit rounding of p, at
+// most ln(1 + 2^-8) for bf16 and ln(1 + 2^-11) for fp16.
+__device__ __forceinline__ float integral_max(float m) { return __builtin_ceilf(m); }
+
+// acc + lo + hi of a packed pair of QT values (one v_dot2c against (1, 1)):
+// the sum of p values exactly as rounded for the PV MFMA.
+template <int QT>
+__device__ __forceinline__ float add_pair(uint32_t pk, float acc) {
+  if constexpr (QT == UA_F16) {
+    return __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, pk),
+                                  __builtin_bit_cast(f16x2, 0x3c003c00u), acc, false);
+  } else {
+    return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, pk),
+                                           __builtin_bit_cast(bf16x2, 0x3f803f80u), acc, false);
+  }
+}
+
 // Load N dwords (N in {1, 2, 4, 8}) from a 4*N-byte aligned address.
 template <int N>
 __device__ __forceinline__ void load_dw(const char* ptr, uint32_t* dst) {
@@ -431,6 +459,8 @@ __global__ __launch_bounds__(64 * kSmallWaves, 2) void small_kernel(Params p) {
   f32x4 oacc[E];
 #pragma unroll
   for (int c = 0; c < E; ++c) oacc[c] = f32x4{0.f, 0.f, 0.f, 0.f};
+  // l: sum of the p as rounded for the PV MFMA (with per-token V scales,
+  // whose PV weights carry the scales: of the unscaled p as computed).
   float m_run = -INFINITY, l_run = 0.0f;
 
   auto compute = [&](const Tile<QT, FP8, D>& t, int i) {
@@ -487,12 +517,12 @@ __global__ __launch_bounds__(64 * kSmallWaves, 2) void small_kernel(Params p) {
     }
     mt = wave_max_xor(mt, 16);
     mt = wave_max_xor(mt, 32);
-    const float m_new = fmaxf(m_run, mt);
+    const float m_new = integral_max(fmaxf(m_run, mt));
     const float m_use = (m_new == -INFINITY) ? 0.0f : m_new;
     const float alpha = fast_exp2(m_run - m_use);
     m_run = m_new;
     u32x4 pb;
-    float psum = 0.0f;
+    float pr = 0.0f;
     if constexpr (tsc) {
       // The PV weights carry the V scales (from lanes 16 g + 8 + 4 hb + r); the
       // softmax sum does not.
@@ -501,18 +531,18 @@ __global__ __launch_bounds__(64 * kSmallWaves, 2) void small_kernel(Params p) {
         const float e0 = fast_exp2(x[2 * q] - m_use), e1 = fast_exp2(x[2 * q + 1] - m_use);
         pb[q] = pack2<QT>(e0 * lane_get(t.sc, 16 * g + 8 + 2 * q),
                           e1 * lane_get(t.sc, 16 * g + 9 + 2 * q));
-        psum += e0 + e1;
+        pr += e0 + e1;
       }
     } else {
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
-        const uint32_t pk =
-            pack2<QT>(fast_exp2(x[2 * q] - m_use), fast_exp2(x[2 * q + 1] - m_use));
+        const float e0 = fast_exp2(x[2 * q] - m_use), e1 = fast_exp2(x[2 * q + 1] - m_use);
+        const uint32_t pk = pack2<QT>(e0, e1);
         pb[q] = pk;
-        psum += lo16<QT>(pk) + hi16<QT>(pk);
+        pr = add_pair<QT>(pk, pr);
       }
     }
-    l_run = l_run * alpha + psum;
+    l_run = l_run * alpha + pr;
 #pragma unroll
     for (int c = 0; c < E; ++c) oacc[c] *= alpha;
 #pragma unroll

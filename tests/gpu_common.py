@@ -1,14 +1,23 @@
 """Helpers shared by the GPU parity tests and smoke(): upload a seeded case,
 run it through the C ABI, compare with the oracle.
 
-Tolerances (max-abs against the float64 oracle; fp8 KV against the oracle on
-the dequantised cache, either e4m3 dialect): fp16 2e-3, bf16 1e-2, fp8 KV 2e-2.  Each element may
-additionally differ by half a unit in the last place of the output type at the
-oracle's value: that is the error of rounding the exact result once to the
-output type, which no kernel can avoid (bf16 half-ULP is 7.8e-3 on [2, 4)).
+Parity gate (max-abs against the float64 oracle; fp8 KV against the oracle on
+the dequantised cache, either e4m3 dialect): fp16 2e-3, bf16 1e-2, fp8 KV 2e-2,
+element by element.  One allowance: an element whose output type is bf16 and
+whose oracle value has |o| >= 2 may additionally differ by half a bf16 unit in
+the last place at that value (7.8e-3 on [2, 4), 1.56e-2 on [4, 8)).  That is the
+error of rounding the exact value once to bf16, which no kernel can avoid, and
+at |o| >= 4 it exceeds the 1e-2 gate on its own.  Every element that needed the
+allowance is counted; fp16 outputs (half-ULP <= 1.95e-3 below 8) and bf16
+outputs below 2 get no allowance.
+
+Every comparison is recorded in RECORDS (label, max-abs, elements, elements
+that needed the allowance); tests/conftest.py prints a per-workload summary at
+the end of the pytest run.
 """
 
 import math
+import os
 
 import numpy as np
 import torch
@@ -96,13 +105,28 @@ def run(case, dev=None, path="auto", n_part=0, lse=False, poison_out=True, ws=No
     return res, l, plan
 
 
+RECORDS = []
+BAND_MIN = 2.0  # |oracle| from which bf16 outputs get the half-ULP allowance
+
+
+def allowed_error(case, ref):
+    """Per-element bound: the dtype's tolerance, plus half a bf16 ULP where the
+    output is bf16 and |ref| >= 2 (the unavoidable rounding of the exact value)."""
+    tol = tolerance(case)
+    allowed = np.full(np.shape(ref), tol)
+    if case["o_dtype"] == "bf16":
+        band = np.abs(ref) >= BAND_MIN
+        allowed = np.where(band, tol + half_ulp(ref, "bf16"), allowed)
+    return allowed
+
+
 def compare(case, got, ref, rows=None, label=""):
-    """Assert |got - ref| <= tol + half_ulp(ref) elementwise; return max-abs error."""
+    """Assert |got - ref| <= allowed_error elementwise; record and return max-abs."""
     if rows is not None:
         got = got[rows]
     tol = tolerance(case)
     err = np.abs(got - ref)
-    allowed = tol + half_ulp(ref, case["o_dtype"])
+    allowed = allowed_error(case, ref)
     bad = ~(err <= allowed)  # NaN counts as bad
     if bad.any():
         idx = np.argwhere(bad)[:5]
@@ -110,7 +134,55 @@ def compare(case, got, ref, rows=None, label=""):
             f"{label}: {int(bad.sum())} elements outside tolerance {tol}; max err "
             f"{np.nanmax(err) if np.isfinite(err).any() else float('nan')}; first "
             f"{[(tuple(i), float(got[tuple(i)]), float(ref[tuple(i)])) for i in idx]}")
-    return float(err.max()) if err.size else 0.0
+    max_abs = float(err.max()) if err.size else 0.0
+    n_band = int(np.count_nonzero(err > tol))
+    RECORDS.append(dict(label=label, max_abs=max_abs, n=int(err.size), n_band=n_band,
+                        tol=tol, o_dtype=case["o_dtype"]))
+    return max_abs
+
+
+def ulp(x, o_dtype):
+    """One unit in the last place of the output type at |x| (subnormal floor)."""
+    return 2.0 * half_ulp(np.where(np.asarray(x) == 0, 1e-30, x), o_dtype)
+
+
+def oracle_parallel(case, rows=None, chunk=256, workers=None):
+    """The oracle on `rows` (default: all query rows), row chunks spread over
+    host threads (every row is independent; numpy's elementwise work and BLAS
+    release the GIL).  BLAS runs one thread per worker meanwhile."""
+    from concurrent.futures import ThreadPoolExecutor
+
+    import oracle
+    total_q = case["q"].shape[0]
+    rows = np.arange(total_q) if rows is None else np.asarray(rows, dtype=np.int64)
+    parts = [rows[i:i + chunk] for i in range(0, len(rows), chunk)]
+    workers = workers or min(16, os.cpu_count() or 1, max(1, len(parts)))
+    try:
+        from threadpoolctl import threadpool_limits
+        limit = threadpool_limits(1)
+    except Exception:  # threadpoolctl missing: BLAS keeps its own threads
+        limit = None
+    try:
+        with ThreadPoolExecutor(workers) as ex:
+            res = list(ex.map(lambda r: oracle.attention(**case, rows=r), parts))
+    finally:
+        if limit is not None:
+            limit.restore_original_limits()
+    if not res:
+        Hq, D = case["q"].shape[1:]
+        return np.zeros((0, Hq, D)), np.zeros((0, Hq))
+    return np.concatenate([o for o, _ in res]), np.concatenate([l for _, l in res])
+
+
+def block_edge_rows(case, block_q):
+    """First and last query row of every query block (blocks of block_q tokens
+    inside each sequence, as the kernels cut them)."""
+    cu = case["cu_seqlens_q"]
+    out = []
+    for s in range(len(cu) - 1):
+        for t0 in range(int(cu[s]), int(cu[s + 1]), block_q):
+            out += [t0, min(t0 + block_q, int(cu[s + 1])) - 1]
+    return np.array(sorted(set(out)), dtype=np.int64)
 
 
 def sample_rows(total_q, n, seed):
@@ -122,8 +194,20 @@ def sample_rows(total_q, n, seed):
     return np.array(sorted(base), dtype=np.int64)
 
 
-def check_lse(got, ref, atol=2e-3, label=""):
-    """LSE (natural log, fp32 on the GPU): same -inf pattern, finite values within atol."""
+def lse_tolerance(case):
+    """The kernels' log-sum-exp is that of the softmax weights as rounded to the
+    query dtype for the P*V product (the normaliser the output is divided by):
+    each weight carries at most half an ULP of relative error, 2^-8 for bf16 and
+    2^-11 for fp16, so the log of their sum is within ln(1 + 2^-8) (resp.
+    ln(1 + 2^-11)) of the exact value, plus 1e-4 for fp32 arithmetic."""
+    return math.log1p(2.0 ** (-8 if case["q_dtype"] == "bf16" else -11)) + 1e-4
+
+
+def check_lse(got, ref, case=None, label="", atol=None):
+    """LSE (natural log, fp32 on the GPU): same -inf pattern, finite values within
+    atol (default: lse_tolerance(case))."""
+    if atol is None:
+        atol = lse_tolerance(case)
     fin = np.isfinite(ref)
     assert np.array_equal(np.isneginf(got), ~fin), f"{label}: -inf pattern of lse differs"
     err = np.abs(got[fin] - ref[fin]).max() if fin.any() else 0.0
