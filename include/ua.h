@@ -58,7 +58,7 @@
 extern "C" {
 #endif
 
-#define UA_ABI_VERSION 4
+#define UA_ABI_VERSION 5
 
 /* UA_FP8_E4M3FN: OCP E4M3 (bias 7, max 448, no inf, NaN = S.1111.111).
  * UA_FP8_E4M3FNUZ: E4M3 with bias 8 (max 240, no inf, no -0, NaN = 0x80). */
@@ -70,7 +70,8 @@ typedef enum {
   UA_EUNSUPPORTED = -2, /* well-formed but not implemented (head size, dtype mix, alignment) */
   UA_EWORKSPACE = -3,   /* workspace missing or smaller than plan->workspace_bytes */
   UA_EHIP = -4,         /* a HIP launch reported an error */
-  UA_EPLAN = -5         /* plan does not belong to this problem, or wrong path for this call */
+  UA_EPLAN = -5,        /* plan does not belong to this problem, or wrong path for this call */
+  UA_ESCRATCH = -6      /* ua_forward_noalloc: plan needs more than UA_NOALLOC_SCRATCH_BYTES */
 } ua_status;
 
 typedef enum { UA_PATH_AUTO = 0, UA_PATH_2D = 1, UA_PATH_SPLITKV = 2 } ua_path;
@@ -240,6 +241,26 @@ const char* ua_status_string(int32_t status);
  */
 ua_status ua_check_inputs(const ua_problem* prob, const ua_args* args, int32_t* flags,
                           void* stream);
+
+/*
+ * ua_forward_noalloc: ua_forward without a caller workspace, for callers that
+ * cannot allocate device memory (code under HIP graph capture, tight serving
+ * loops, harnesses that forbid hipMalloc).  Same problem, plan and arguments
+ * as ua_forward; the one-pass path runs as ua_forward_2d; the split-KV path
+ * keeps its partition states in a static device array of the library,
+ * UA_NOALLOC_SCRATCH_BYTES per GPU, held until the process ends (looked up
+ * once per device on the first call there).  Allocates nothing.
+ *   Returns UA_ESCRATCH (nothing launched) when plan->workspace_bytes exceeds
+ *   UA_NOALLOC_SCRATCH_BYTES: use ua_forward with a workspace, or a plan with
+ *   fewer partitions.  UA_EINVAL when `stream` is not on the current device.
+ *   Other statuses as ua_forward.
+ * Every call on one GPU shares that GPU's array: calls that overlap in time
+ * on one GPU (two streams, two threads) race and give undefined results.
+ * The array keeps the last call's contents; nothing in it needs clearing.
+ */
+#define UA_NOALLOC_SCRATCH_BYTES (64ull << 20)
+ua_status ua_forward_noalloc(const ua_problem* prob, const ua_plan_t* plan, const ua_args* args,
+                             void* stream);
 
 /* UA_ABI_VERSION of the built library. */
 int32_t ua_abi_version(void);

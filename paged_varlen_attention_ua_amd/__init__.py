@@ -7,8 +7,8 @@ binding over it.
 
 from .binding import (UA_BF16, UA_F16, UA_FP8_E4M3FN, UA_PATH_2D, UA_PATH_AUTO,  # noqa: F401
                       UA_PATH_SPLITKV, UaArgs, UaError, UaPlan, UaProblem, lib, ua_abi_version,
-                      ua_forward_2d, ua_forward_splitkv, ua_plan, ua_reduce,
-                      ua_workspace_acc_offset)
+                      ua_forward_2d, ua_forward_noalloc, ua_forward_splitkv, ua_plan,
+                      ua_reduce, ua_workspace_acc_offset)
 
 
 def forward(*args, **kwargs):

@@ -73,7 +73,11 @@ _lib = None
 _lib_lock = threading.Lock()
 
 EXPORTS = ["ua_plan", "ua_forward_2d", "ua_forward_splitkv", "ua_reduce", "ua_forward",
-           "ua_workspace_acc_offset", "ua_status_string", "ua_check_inputs", "ua_abi_version"]
+           "ua_workspace_acc_offset", "ua_status_string", "ua_check_inputs", "ua_abi_version",
+           "ua_forward_noalloc"]
+UA_ESCRATCH = -6
+# Bytes of the library's static split-KV scratch per GPU (ua_forward_noalloc).
+UA_NOALLOC_SCRATCH_BYTES = 64 << 20
 
 
 def lib():
@@ -110,6 +114,9 @@ def lib():
             L.ua_check_inputs.argtypes = [P(UaProblem), P(UaArgs), ctypes.c_void_p,
                                           ctypes.c_void_p]
             L.ua_check_inputs.restype = ctypes.c_int32
+            L.ua_forward_noalloc.argtypes = [P(UaProblem), P(UaPlan), P(UaArgs),
+                                             ctypes.c_void_p]
+            L.ua_forward_noalloc.restype = ctypes.c_int32
             L.ua_abi_version.argtypes = []
             L.ua_abi_version.restype = ctypes.c_int32
             _lib = L
@@ -144,6 +151,12 @@ def ua_forward_splitkv(problem, plan, args, workspace_ptr, workspace_bytes, stre
 def ua_check_inputs(problem, args, flags_ptr, stream=None):
     _check("ua_check_inputs", lib().ua_check_inputs(ctypes.byref(problem), ctypes.byref(args),
                                                     flags_ptr, stream))
+
+
+def ua_forward_noalloc(problem, plan, args, stream=None):
+    """The planned path with the library's static split-KV scratch (no workspace)."""
+    _check("ua_forward_noalloc", lib().ua_forward_noalloc(
+        ctypes.byref(problem), ctypes.byref(plan), ctypes.byref(args), stream))
 
 
 def ua_reduce(problem, plan, args, workspace_ptr, workspace_bytes, stream=None):

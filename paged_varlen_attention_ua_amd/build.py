@@ -23,6 +23,7 @@ SOURCES = [
     ("ua_large.hip", "ua_large_bf16.o", ["-DUA_QT=1"]),
     ("ua_reduce.hip", "ua_reduce.o", []),
     ("ua_check.hip", "ua_check.o", []),
+    ("ua_noalloc.hip", "ua_noalloc.o", []),
 ]
 ARCH = "gfx950"
 

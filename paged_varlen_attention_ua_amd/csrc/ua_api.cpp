@@ -216,6 +216,9 @@ const char* ua_status_string(int32_t s) {
     case UA_EWORKSPACE: return "workspace missing or too small";
     case UA_EHIP: return "HIP launch error";
     case UA_EPLAN: return "plan does not match the problem or the call";
+    case UA_ESCRATCH:
+      return "split-KV workspace of the plan exceeds UA_NOALLOC_SCRATCH_BYTES (use ua_forward "
+             "with a caller workspace)";
     default: return "unknown status";
   }
 }
@@ -421,3 +424,13 @@ ua_status ua_forward(const ua_problem* prob, const ua_plan_t* plan, const ua_arg
 }
 
 }  // extern "C"
+
+namespace ua {
+// Host checks of a split-KV call (plan, problem and argument pointers), as
+// ua_forward_splitkv makes them before it needs the workspace.
+ua_status check_split_call(const ua_problem* prob, const ua_plan_t* plan, const ua_args* args) {
+  ua_status st = check_plan(prob, plan, UA_PATH_SPLITKV);
+  if (st != UA_OK) return st;
+  return check_args(prob, args);
+}
+}  // namespace ua

@@ -107,6 +107,7 @@ inline hipError_t launch_large(const Params& p, int q_dtype, int kv_fmt, int hea
              ? launch_large_f16(p, kv_fmt, head_dim, split, eight_waves, grid, stream)
              : launch_large_bf16(p, kv_fmt, head_dim, split, eight_waves, grid, stream);
 }
+ua_status check_split_call(const ua_problem* prob, const ua_plan_t* plan, const ua_args* args);
 hipError_t launch_reduce(const Params& p, int o_dtype, int head_dim, hipStream_t stream);
 hipError_t launch_check(const ua_problem* p, const ua_args* a, int32_t* flags,
                         hipStream_t stream);

@@ -33,7 +33,7 @@ def test_library_exports_every_declared_symbol():
     lib = ctypes.CDLL(B.LIB_PATH)
     for fn in _declared_functions():
         assert hasattr(lib, fn), fn
-    assert U.ua_abi_version() == 4
+    assert U.ua_abi_version() == 5
 
 
 def test_struct_sizes_match_header_layout():
@@ -252,3 +252,28 @@ def test_empty_batch_is_a_no_op():
 def test_status_strings():
     assert B.lib().ua_status_string(0) == b"ok"
     assert B.lib().ua_status_string(-3).startswith(b"workspace")
+
+
+def test_noalloc_refuses_before_touching_the_device():
+    """ua_forward_noalloc checks the call on the host first: a missing plan or
+    pointers, a plan of another problem, and a split plan whose workspace
+    exceeds the static scratch (UA_ESCRATCH) all return before any HIP call."""
+    L = B.lib()
+    p = problem()
+    args = B.UaArgs()
+    assert L.ua_forward_noalloc(ctypes.byref(p), None, ctypes.byref(args), None) == -1
+    st, plan = status_of(p, force_path=B.UA_PATH_SPLITKV, n_part=4)
+    assert st == 0 and plan.workspace_bytes <= B.UA_NOALLOC_SCRATCH_BYTES
+    assert L.ua_forward_noalloc(ctypes.byref(p), ctypes.byref(plan), ctypes.byref(args),
+                                None) == -1  # null device pointers
+    assert L.ua_forward_noalloc(ctypes.byref(problem(window=100)), ctypes.byref(plan),
+                                ctypes.byref(args), None) == -5
+    for f in ("q", "k_cache", "v_cache", "block_table", "cu_seqlens_q", "seq_lens", "out"):
+        setattr(args, f, 1 << 20)  # fake aligned pointers: nothing may launch
+    big = problem(num_seqs=1, total_q=8192, max_seqlen_q=8192, max_seqlen_k=8192, window=0,
+                  num_blocks=1200, max_blocks_per_seq=600)
+    st, plan = status_of(big, force_path=B.UA_PATH_SPLITKV, n_part=4)
+    assert st == 0 and plan.workspace_bytes > B.UA_NOALLOC_SCRATCH_BYTES
+    assert L.ua_forward_noalloc(ctypes.byref(big), ctypes.byref(plan), ctypes.byref(args),
+                                None) == B.UA_ESCRATCH
+    assert L.ua_status_string(B.UA_ESCRATCH).startswith(b"split-KV workspace")
