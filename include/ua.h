@@ -133,7 +133,9 @@ typedef struct {
   int32_t n_part;           /* key-range partitions per query block (1 for 2D) */
   int32_t grid_x, grid_y, grid_z; /* grid_y = kv heads x head groups (small kernel: decode
                                      with G > 16 splits a kv head's query heads) */
-  int32_t flags;            /* bit 0: one query block per sequence (block x = sequence) */
+  int32_t flags;            /* bit 0: one query block per sequence (block x = sequence);
+                               bit 1: rank order (block x = block n_s - 1 - x / num_seqs
+                               of sequence x % num_seqs: heaviest blocks first) */
   uint64_t workspace_bytes; /* bytes ua_forward_splitkv needs; 0 for 2D */
   uint64_t problem_hash;    /* ties the plan to the ua_problem it was made for */
 } ua_plan_t;

@@ -22,11 +22,14 @@ _WS = {}
 _WS_LOCK = threading.Lock()
 
 
-def num_cus(device):
+def device_cus(device):
     idx = device.index if device.index is not None else torch.cuda.current_device()
     if idx not in _NUM_CUS:
         _NUM_CUS[idx] = torch.cuda.get_device_properties(idx).multi_processor_count
     return _NUM_CUS[idx]
+
+
+num_cus = device_cus
 
 
 def make_problem(q, k_cache, v_cache, block_table, *, num_seqs, max_seqlen_q, max_seqlen_k,
@@ -118,13 +121,19 @@ def make_args(q, k_cache, v_cache, block_table, cu_seqlens_q, seq_lens, out, lse
 
 
 def workspace(nbytes, device, stream):
-    """Grow-only fp32 workspace per (device, stream); old buffers stay alive."""
+    """Grow-only workspace per (device, stream).  Sizes are rounded up to a power
+    of two, so a slowly growing demand reallocates O(log) times; replaced buffers
+    stay alive (a captured graph may still point at one), and since sizes at
+    least double, all of them together are smaller than the current buffer."""
     key = (device.index, int(stream.cuda_stream))
     with _WS_LOCK:
         buf = _WS.get(key)
         if buf is None or buf.numel() < nbytes:
-            buf = torch.empty(max(int(nbytes), 256), dtype=torch.uint8, device=device)
-            _WS.setdefault(("retired",) + key, []).append(_WS.get(key))
+            size = 1 << max(8, (max(int(nbytes), 1) - 1).bit_length())
+            old = _WS.get(key)
+            if old is not None:
+                _WS.setdefault(("retired",) + key, []).append(old)
+            buf = torch.empty(size, dtype=torch.uint8, device=device)
             _WS[key] = buf
     return buf
 
@@ -132,11 +141,12 @@ def workspace(nbytes, device, stream):
 def forward(q, k_cache, v_cache, block_table, cu_seqlens_q, seq_lens, *, max_seqlen_q,
             max_seqlen_k, scale, softcap=0.0, window=0, k_scale=1.0, v_scale=1.0,
             alibi_slopes=None, sinks=None, out=None, lse=None, path="auto", n_part=0,
-            ws=None, qq_bias=None, k_token_scales=None, v_token_scales=None):
+            ws=None, qq_bias=None, k_token_scales=None, v_token_scales=None, num_cus=None):
     """Unified paged varlen attention; returns (out, plan).
 
     path: "auto" (dispatcher), "2d" (one pass) or "splitkv" (partitions + reduce).
     n_part: forced partition count for the split path (0 = automatic).
+    num_cus: compute units the planner assumes (default: the device's).
     """
     if not q.is_cuda:
         raise ValueError("q must be a GPU tensor")
@@ -148,7 +158,8 @@ def forward(q, k_cache, v_cache, block_table, cu_seqlens_q, seq_lens, *, max_seq
                         softcap=softcap, window=window, k_scale=k_scale, v_scale=v_scale,
                         alibi_slopes=alibi_slopes, sinks=sinks, out=out, qq_bias=qq_bias,
                         k_token_scales=k_token_scales, v_token_scales=v_token_scales)
-    plan = B.ua_plan(prob, num_cus(q.device), _PATH[path], n_part)
+    plan = B.ua_plan(prob, num_cus if num_cus is not None else device_cus(q.device),
+                     _PATH[path], n_part)
     args = make_args(q, k_cache, v_cache, block_table, cu_seqlens_q, seq_lens, out, lse,
                      alibi_slopes, sinks, qq_bias, k_token_scales, v_token_scales)
     stream = torch.cuda.current_stream(q.device)

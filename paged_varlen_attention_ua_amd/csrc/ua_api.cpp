@@ -199,6 +199,7 @@ Params make_params(const ua_problem* p, const ua_plan_t* plan, const ua_args* a,
   }
   q.v_scale = fp8 ? (float)((double)p->v_scale * half) : 1.0f;
   q.seq_blocks = plan->flags & 1;
+  q.rank_order = (plan->flags >> 1) & 1;
   return q;
 }
 
@@ -319,6 +320,27 @@ ua_status ua_plan(const ua_problem* prob, int32_t num_cus, int32_t force_path,
   if (prob->max_seqlen_q <= bq) {
     plan->flags |= 1;
     plan->grid_x = prob->num_seqs;
+  }
+  // Rank order for large blocks when the grid takes more than one round of
+  // the device's workgroup slots: slot x is block n_s - 1 - x / num_seqs of
+  // sequence x % num_seqs, so workgroups start heaviest-first across all
+  // sequences (under a causal mask a sequence's later blocks walk more keys),
+  // the order that lets later, lighter blocks fill the gaps.  It needs
+  // num_seqs * max_blocks slots (slots past a sequence's block count exit at
+  // once), so it is used only when that is at most 1.5 x the packed count.
+  // Measured on MI355X: 4 x 1k causal prompts 498 -> 521 TFLOP/s (the packed
+  // order ran each sequence's blocks heaviest-first, but sequence by sequence,
+  // so the first sequence's heavy blocks started last); other prefills
+  // unchanged.
+  {
+    const int64_t per_cu = eight ? 1 : (prob->head_dim > 128 ? 1 : 2);
+    const int64_t max_nb = ceil_div(prob->max_seqlen_q, bq);
+    const int64_t ranked = (int64_t)prob->num_seqs * max_nb;
+    if (!small && !(plan->flags & 1) && ranked * prob->num_kv_heads * n_part > per_cu * num_cus &&
+        2 * ranked <= 3 * slots && ranked <= 0x7fffffff) {
+      plan->flags |= 2;
+      plan->grid_x = (int32_t)ranked;
+    }
   }
   plan->grid_y = prob->num_kv_heads * HG;
   plan->grid_z = n_part;

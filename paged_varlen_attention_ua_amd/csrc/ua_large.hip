@@ -222,7 +222,9 @@ __global__ __launch_bounds__(64 * NW, (large_min_groups<D, NW, FP8 && TS>())) vo
 
   // XCD-aware order: consecutive logical blocks (the query blocks of one kv
   // head and partition, which read the same K/V) stay on one XCD; heavier
-  // (later) query blocks go first.
+  // (later) query blocks go first (p.rank_order: logical block x is block
+  // n_s - 1 - x / num_seqs of sequence x % num_seqs, so the last, heaviest
+  // block of every sequence is dispatched before any sequence's second-last).
   const int gx = gridDim.x, gy = gridDim.y;
   const int nwg = gx * gy * gridDim.z;
   int lin = blockIdx.x + gx * (blockIdx.y + gy * blockIdx.z);
@@ -232,7 +234,14 @@ __global__ __launch_bounds__(64 * NW, (large_min_groups<D, NW, FP8 && TS>())) vo
   const int part = lin / (gx * gy);
 
   int s, tok0;
-  if (p.seq_blocks) {
+  if (p.rank_order) {
+    const int r = lin % gx;  // rank from the end of the sequence: 0 first
+    s = r % p.num_seqs;
+    const int qs = p.cu_seqlens_q[s];
+    const int nb = (p.cu_seqlens_q[s + 1] - qs + p.block_q - 1) / p.block_q;
+    tok0 = qs + (nb - 1 - r / p.num_seqs) * p.block_q;  // r / num_seqs >= nb: no block
+    if (r / p.num_seqs >= nb) return;
+  } else if (p.seq_blocks) {
     s = qb;
     tok0 = p.cu_seqlens_q[s];
   } else {

@@ -78,7 +78,7 @@ def to_device(case, device="cuda"):
 
 
 def run(case, dev=None, path="auto", n_part=0, lse=False, poison_out=True, ws=None,
-        out=None):
+        out=None, num_cus=None):
     """Run one case on the GPU through the C ABI; returns (out fp64 numpy, lse, plan)."""
     import paged_varlen_attention_ua_amd.attention as A
     dev = dev or to_device(case)
@@ -98,7 +98,7 @@ def run(case, dev=None, path="auto", n_part=0, lse=False, poison_out=True, ws=No
                         alibi_slopes=dev["alibi_slopes"], sinks=dev["sinks"], out=out,
                         lse=lse_t, path=path, n_part=n_part, ws=ws, qq_bias=dev.get("qq_bias"),
                         k_token_scales=dev.get("k_token_scales"),
-                        v_token_scales=dev.get("v_token_scales"))
+                        v_token_scales=dev.get("v_token_scales"), num_cus=num_cus)
     torch.cuda.synchronize()
     res = o.float().cpu().numpy().astype(np.float64)
     l = lse_t.cpu().numpy().astype(np.float64) if lse_t is not None else None

@@ -668,3 +668,23 @@ def test_hand_example_on_gpu(name, dts):
         compare(case, got, exp, label=f"hand-{name}-{dts[0]}-{dts[1]}/{path}")
         if lse_exp is not None:
             check_lse(lse[:, :1], np.array([[lse_exp]]), case, label=f"hand-{name}-lse")
+
+
+@pytest.mark.parametrize("seqs,kw", [
+    ([(100, 100), (32, 32)], {}),
+    ([(33, 40), (64, 64), (5, 9), (31, 31)], {}),
+    ([(300, 300), (129, 200)], dict(window=64)),
+    ([(100, 100), (100, 150), (32, 32), (64, 64), (31, 31), (100, 100)], dict(sinks=True)),
+    ([(120, 130), (97, 97)], dict(head_dim=256)),
+    ([(300, 4400), (300, 4300)], {}),  # 256-row (eight-wave) blocks
+])
+def test_rank_order_batches(seqs, kw):
+    """Large blocks dispatched in rank order (heaviest block of every sequence
+    first; forced here by planning for a one-CU device): one pass and split."""
+    case = make_case(seqs=seqs, seed=160 + len(seqs), **dict(BASE, **kw))
+    ref, ref_lse = oracle.attention(**case)
+    for path, n_part in (("2d", 0), ("splitkv", 3)):
+        got, lse, plan = run(case, path=path, n_part=n_part, lse=True, num_cus=1)
+        assert plan.kernel != 0 and plan.flags & 2, (plan.kernel, plan.flags)
+        compare(case, got, ref, label=f"rank-{len(seqs)}-{path}")
+        check_lse(lse, ref_lse, case, label="rank")
