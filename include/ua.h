@@ -135,7 +135,11 @@ typedef struct {
                                      with G > 16 splits a kv head's query heads) */
   int32_t flags;            /* bit 0: one query block per sequence (block x = sequence);
                                bit 1: rank order (block x = block n_s - 1 - x / num_seqs
-                               of sequence x % num_seqs: heaviest blocks first) */
+                               of sequence x % num_seqs: heaviest blocks first);
+                               bit 2: wave per row block (small kernel: each wave of
+                               a workgroup owns one of grid_y's row blocks and walks
+                               the whole partition; needs grid_y % 4 == 0 and
+                               block_size % 16 == 0, else calls return UA_EPLAN) */
   uint64_t workspace_bytes; /* bytes ua_forward_splitkv needs; 0 for 2D */
   uint64_t problem_hash;    /* ties the plan to the ua_problem it was made for */
 } ua_plan_t;

@@ -17,6 +17,7 @@ UA_F16, UA_BF16, UA_FP8_E4M3FN, UA_FP8_E4M3FNUZ = 0, 1, 2, 3
 UA_PATH_AUTO, UA_PATH_2D, UA_PATH_SPLITKV = 0, 1, 2
 UA_CHECK_BITS = {1: "cu_seqlens_q", 2: "q_len", 4: "kv_len", 8: "block_table"}
 UA_OK = 0
+UA_EPLAN = -5
 
 
 class UaError(RuntimeError):

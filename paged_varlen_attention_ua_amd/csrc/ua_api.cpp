@@ -200,6 +200,7 @@ Params make_params(const ua_problem* p, const ua_plan_t* plan, const ua_args* a,
   q.v_scale = fp8 ? (float)((double)p->v_scale * half) : 1.0f;
   q.seq_blocks = plan->flags & 1;
   q.rank_order = (plan->flags >> 1) & 1;
+  q.head_waves = (plan->flags >> 2) & 1;
   return q;
 }
 
@@ -273,18 +274,34 @@ ua_status ua_plan(const ua_problem* prob, int32_t num_cus, int32_t force_path,
   const int64_t est_blocks =
       std::min<int64_t>(slots, (int64_t)prob->num_seqs * ceil_div(prob->max_seqlen_q, bq));
   if (prob->window > 0) eff_k = std::min<int64_t>(eff_k, (int64_t)prob->window + bq - 1);
-  const int64_t wgs = est_blocks * prob->num_kv_heads * HG;
+  const int64_t wgs_rb = est_blocks * prob->num_kv_heads * HG;  // one per row block
+  // Small blocks split when the row blocks do not fill the device and the
+  // range is long; stay one-pass for short ranges.
+  const bool small_split = small && wgs_rb > 0 && wgs_rb < num_cus && eff_k > 1024;
+  // Wave per row block (a multiple of four row blocks, i.e. kv heads x head
+  // groups, and 16-slot-aligned cache blocks): each wave owns one row block and
+  // walks the whole partition, the four waves of a workgroup reading adjacent
+  // kv heads' rows of the same cache slots.  Used where the small blocks split
+  // anyway (the partition count then grows four-fold to keep the wave count)
+  // or where even a quarter of the workgroups fills the device four times.
+  const bool head_waves = small && (prob->num_kv_heads * HG) % kSmallWaves == 0 &&
+                          prob->block_size % 16 == 0 &&
+                          (small_split || wgs_rb >= (int64_t)kSmallWaves * num_cus);
+  const int64_t wgs = head_waves ? wgs_rb / kSmallWaves : wgs_rb;
 
   // Automatic partition count: fill the device with small workgroups, keep at
   // least two tiles per partition, and stay one-pass for short ranges.
   int auto_parts = 1;
-  if (small && wgs > 0 && wgs < num_cus && eff_k > 1024) {
+  if (small_split) {
     // Measured on MI355X: about one small workgroup per CU for 16-bit KV and two
-    // for fp8 KV (half the bytes per key).  At least 64 keys per partition:
-    // decode of a few sequences is latency-bound, and 32 partitions of its
-    // 4096-key or 2048-key (d256) ranges ran 7% and 24% faster than the 16 and
-    // 8 that a 256-key minimum gave.
-    const int64_t per_cu = is_fp8(prob->kv_dtype) ? 2 : 1;
+    // for fp8 KV (half the bytes per key); one for both with a wave per row
+    // block (long decode, 8 x 8 row blocks: 16 partitions 33.1 us per step
+    // against 35.2 at 32; fp8 cache 24.4 against 24.7; partition counts that
+    // leave 1.5 workgroups per CU ran 10-13% slower).  At least 64 keys per
+    // partition: decode of a few sequences is latency-bound, and 32 partitions
+    // of its 4096-key or 2048-key (d256) ranges ran 7% and 24% faster than the
+    // 16 and 8 that a 256-key minimum gave.
+    const int64_t per_cu = (is_fp8(prob->kv_dtype) && !head_waves) ? 2 : 1;
     const int64_t want = ceil_div(per_cu * num_cus, wgs);
     const int64_t by_len = std::max<int64_t>(1, eff_k / 64);
     auto_parts = (int)std::max<int64_t>(1, std::min<int64_t>(std::min(want, by_len), 64));
@@ -342,6 +359,7 @@ ua_status ua_plan(const ua_problem* prob, int32_t num_cus, int32_t force_path,
       plan->grid_x = (int32_t)ranked;
     }
   }
+  if (head_waves) plan->flags |= 4;
   plan->grid_y = prob->num_kv_heads * HG;
   plan->grid_z = n_part;
   plan->workspace_bytes =
@@ -368,6 +386,11 @@ static ua_status check_plan(const ua_problem* prob, const ua_plan_t* plan, int32
   if (plan->grid_y < prob->num_kv_heads || plan->grid_y % prob->num_kv_heads != 0 ||
       (prob->num_q_heads / prob->num_kv_heads) % (plan->grid_y / prob->num_kv_heads) != 0 ||
       (plan->kernel != 0 && plan->grid_y != prob->num_kv_heads))
+    return UA_EPLAN;
+  // Wave per row block: small kernel, whole workgroups of row blocks, cache
+  // blocks of whole 16-slot halves.
+  if ((plan->flags & 4) &&
+      (plan->kernel != 0 || plan->grid_y % kSmallWaves != 0 || prob->block_size % 16 != 0))
     return UA_EPLAN;
   return UA_OK;
 }

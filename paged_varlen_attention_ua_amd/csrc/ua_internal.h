@@ -81,6 +81,7 @@ struct Params {
   int32_t head_groups;  // blocks per kv head along y (small kernel; 1 otherwise)
   int32_t group_rows;   // query heads per block and token: group / head_groups
   int32_t rank_order;   // 1: block x is block n_s - 1 - x / num_seqs of sequence x % num_seqs
+  int32_t head_waves;   // 1: small kernel, the waves of a workgroup take consecutive row blocks
 };
 
 // Storage format of the K/V cache as the kernels see it.

@@ -1,17 +1,18 @@
 // Small-query-block attention kernel for gfx950: decode and split-KV partitions.
 //
-// One workgroup owns (query block, kv head, key partition).  A query block is
-// block_q consecutive query tokens of one sequence times the G = Hq / Hkv query
-// heads that share the kv head (grouped-query packing: every row of the block
-// reads the same K/V rows), at most 16 rows: the N side of a 16x16x32 MFMA.
-// Decode with G > 16 (e.g. multi-query attention) splits the G heads into
-// groups of at most 16, one block each, which read the same K/V rows.
-// The four waves of the workgroup walk interleaved 32-key tiles of the
-// partition, each keeping its own online-softmax state (running max m, sum l
-// and output accumulator, AITER PR #3962 review diff), and merge through LDS at
-// the end.  With one partition the block writes the final rows (the one-pass
-// form of the RocKE README, "Why three tables"); otherwise it writes the
-// partition's (m, l, acc) for ua_reduce.
+// A row block is block_q consecutive query tokens of one sequence times the
+// G = Hq / Hkv query heads that share a kv head (grouped-query packing: every
+// row of the block reads the same K/V rows), at most 16 rows: the N side of a
+// 16x16x32 MFMA.  Decode with G > 16 (e.g. multi-query attention) splits the G
+// heads into groups of at most 16, one row block each, which read the same K/V
+// rows.  A workgroup of four waves owns (query block, key partition) and
+// either one row block, whose interleaved 32-key tiles the four waves share
+// (each keeping its own online-softmax state: running max m, sum l and output
+// accumulator, AITER PR #3962 review diff, merged through LDS at the end), or
+// four consecutive row blocks, one per wave, each walking every tile of the
+// partition (wave per row block, see small_kernel).  With one partition the
+// block writes the final rows (the one-pass form of the RocKE README, "Why
+// three tables"); otherwise it writes the partition's (m, l, acc) for ua_reduce.
 //
 // Data flow per 32-key tile and wave (K/V data never pass through LDS):
 //   * K rows go straight from HBM into registers already in the MFMA A-operand
@@ -45,7 +46,8 @@ namespace {
 // Running maxima of the online softmax (base-2 logit units) are kept at whole
 // numbers: the maximum m a row's p = 2^(x - m) are formed against is rounded
 // up to an integer.  p <= 1 still holds at the row maximum, but the mantissa
-// of p is then 2^frac(x) whatever m is, so the 16-bit rounding of p before
+// of p is then that of 2^(x - rint(x)) whatever m is (p is formed as that
+// value times an exact power of two), so the 16-bit rounding of p before
 // the PV MFMA is the same in every partition, wave or tile order, and every
 // rescale factor 2^(m_old - m_new) (and each partition's weight in the merge)
 // is an exact power of two: split and one-pass results differ only by the
@@ -281,23 +283,34 @@ __device__ __forceinline__ float lane_get(float v, int src) {
   return __builtin_bit_cast(float, __builtin_amdgcn_ds_bpermute(4 * src, __builtin_bit_cast(int, v)));
 }
 
-template <int QT, bool FP8, int D, bool SPLIT, bool PAGE16, bool FNUZ, bool TS>
+// HW (wave per row block): the four waves of a workgroup own four consecutive
+// row blocks (unit u = kv head x head groups + group, u = 4 blockIdx.y + wave),
+// each walking every tile of the partition, so at any time they read the same
+// cache slots of adjacent kv heads: with the usual [block][slot][head][dim]
+// cache layout that is one contiguous run of 4 head rows per slot instead of
+// one head row (measured on MI355X with a load-only kernel over that layout:
+// fp8 rows 4.0-4.3 -> 4.5-5.0 TB/s, 16-bit rows 4.9 -> 5.1 TB/s).  The waves
+// share the staged block-table entries and need no merge.  Otherwise the four
+// waves of a workgroup share one row block and interleave its tiles.
+template <int QT, bool FP8, int D, bool SPLIT, bool PAGE16, bool FNUZ, bool TS, bool HW>
 __global__ __launch_bounds__(64 * kSmallWaves, 2) void small_kernel(Params p) {
   using C = SmallCfg<QT, FP8, D>;
   constexpr int E = C::E;
   constexpr int QC = C::QC;
   constexpr int DQ = C::DQ;
-  constexpr int kStride = kSmallTile * kSmallWaves;
+  static_assert(!HW || PAGE16, "wave-per-row-block mode stages the block table");
+  constexpr int kStride = HW ? kSmallTile : kSmallTile * kSmallWaves;
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int g = lane >> 4, r16 = lane & 15;
   const int qb = blockIdx.x, part = blockIdx.z;
-  // blockIdx.y = kv head x head groups + group: decode with G > 16 splits a kv
-  // head's query heads into head_groups groups of group_rows heads, one block each.
+  // Row block: kv head x head groups + group; decode with G > 16 splits a kv
+  // head's query heads into head_groups groups of group_rows heads.
+  const int unit = HW ? (int)blockIdx.y * kSmallWaves + wave : (int)blockIdx.y;
   const int HG = p.head_groups;
-  const int kvh = HG == 1 ? (int)blockIdx.y : (int)blockIdx.y / HG;
-  const int hg = (int)blockIdx.y - kvh * HG;
+  const int kvh = HG == 1 ? unit : unit / HG;
+  const int hg = unit - kvh * HG;
 
   int s, tok0;
   if (p.seq_blocks) {
@@ -332,9 +345,10 @@ __global__ __launch_bounds__(64 * kSmallWaves, 2) void small_kernel(Params p) {
   if (k0 >= k1) {
     // Empty partition: l = 0 tells the reduce to skip it.
     if constexpr (SPLIT) {
-      if (tid < 16) {
-        const int rt = tid / G, rh = tid - (tid / G) * G;
-        if (tid < p.block_q * G && rt < ntok) {
+      const int t16 = HW ? lane : tid;  // HW: every wave writes its own rows
+      if (t16 < 16) {
+        const int rt = t16 / G, rh = t16 - (t16 / G) * G;
+        if (t16 < p.block_q * G && rt < ntok) {
           const int64_t row = (int64_t)(tok0 + rt) * p.num_q_heads + hbase + rh;
           p.ws_l[(int64_t)part * R + row] = 0.0f;
           p.ws_m[(int64_t)part * R + row] = -INFINITY;
@@ -345,24 +359,30 @@ __global__ __launch_bounds__(64 * kSmallWaves, 2) void small_kernel(Params p) {
   }
 
   // This wave's tiles: kt = wk0 + kStride * i, i < nt.
-  const int wk0 = k0 + kSmallTile * wave;
+  const int wk0 = HW ? k0 : k0 + kSmallTile * wave;
   const int nt = wk0 < k1 ? (k1 - wk0 + kStride - 1) / kStride : 0;
   const int32_t* bt_row = p.block_table + (int64_t)s * p.max_blocks_per_seq;
 
-  // Block-table entries of this wave's first kPreTiles tiles, staged in the
-  // wave's own LDS slice: entry 2i + hb is the block of tile i, half hb (-1 when
+  // Block-table entries of this wave's first kPreTiles tiles, staged in LDS
+  // (the wave's own slice; HW: one copy for the whole workgroup, whose waves
+  // walk the same tiles): entry 2i + hb is the block of tile i, half hb (-1 when
   // the half has no loadable key).  Reading them later waits only on LDS, never
   // on the tile loads in flight.
-  constexpr int kPreTiles = 256;
-  __shared__ int32_t sm_pg[kSmallWaves][2 * kPreTiles];
+  constexpr int kPreTiles = HW ? 256 * kSmallWaves : 256;
+  __shared__ int32_t sm_pg_all[kSmallWaves * 2 * 256];
+  int32_t* sm_pg = HW ? sm_pg_all : sm_pg_all + wave * 2 * kPreTiles;
   auto entry = [&](int j) -> int32_t {
     const int i = j >> 1;
     const int kb0 = wk0 + kStride * i + 16 * (j & 1);
     return (kb0 < k1 && kb0 + 16 > kl) ? bt_row[fastdiv((uint32_t)kb0, p.bs_div)] : -1;
   };
-  if constexpr (PAGE16) {
+  if constexpr (HW) {
     const int ne = 2 * min(nt, kPreTiles);
-    for (int j = lane; j < ne; j += 64) sm_pg[wave][j] = entry(j);
+    for (int j = tid; j < ne; j += 64 * kSmallWaves) sm_pg[j] = entry(j);
+    __syncthreads();
+  } else if constexpr (PAGE16) {
+    const int ne = 2 * min(nt, kPreTiles);
+    for (int j = lane; j < ne; j += 64) sm_pg[j] = entry(j);
   }
 
   // This lane's query row.
@@ -428,8 +448,8 @@ __global__ __launch_bounds__(64 * kSmallWaves, 2) void small_kernel(Params p) {
 
   auto tile_pages = [&](int i, int32_t* page) __attribute__((always_inline)) {
     if (i < kPreTiles) {
-      page[0] = __builtin_amdgcn_readfirstlane(sm_pg[wave][2 * i]);
-      page[1] = __builtin_amdgcn_readfirstlane(sm_pg[wave][2 * i + 1]);
+      page[0] = __builtin_amdgcn_readfirstlane(sm_pg[2 * i]);
+      page[1] = __builtin_amdgcn_readfirstlane(sm_pg[2 * i + 1]);
     } else {
       page[0] = entry(2 * i);
       page[1] = entry(2 * i + 1);
@@ -521,6 +541,16 @@ __global__ __launch_bounds__(64 * kSmallWaves, 2) void small_kernel(Params p) {
     const float m_use = (m_new == -INFINITY) ? 0.0f : m_new;
     const float alpha = fast_exp2(m_run - m_use);
     m_run = m_new;
+    // p = 2^(x - m) as 2^(x - rint(x)) scaled by 2^(rint(x) - m) (ldexp, exact):
+    // x - rint(x) is exact for every float while x - m is not (|x| < 1 < m), so
+    // p's mantissa depends on x alone, never on the running maximum.  Masked
+    // keys (-inf) and keys more than 200 below m give 0.
+    const float x_lo = m_use - 200.0f;
+    auto pexp = [&](float xv) __attribute__((always_inline)) {
+      const float xc = fmaxf(xv, x_lo);
+      const float kx = __builtin_rintf(xc);
+      return __builtin_amdgcn_ldexpf(fast_exp2(xc - kx), (int)(kx - m_use));
+    };
     u32x4 pb;
     float pr = 0.0f;
     if constexpr (tsc) {
@@ -528,7 +558,7 @@ __global__ __launch_bounds__(64 * kSmallWaves, 2) void small_kernel(Params p) {
       // softmax sum does not.
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
-        const float e0 = fast_exp2(x[2 * q] - m_use), e1 = fast_exp2(x[2 * q + 1] - m_use);
+        const float e0 = pexp(x[2 * q]), e1 = pexp(x[2 * q + 1]);
         pb[q] = pack2<QT>(e0 * lane_get(t.sc, 16 * g + 8 + 2 * q),
                           e1 * lane_get(t.sc, 16 * g + 9 + 2 * q));
         pr += e0 + e1;
@@ -536,15 +566,19 @@ __global__ __launch_bounds__(64 * kSmallWaves, 2) void small_kernel(Params p) {
     } else {
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
-        const float e0 = fast_exp2(x[2 * q] - m_use), e1 = fast_exp2(x[2 * q + 1] - m_use);
+        const float e0 = pexp(x[2 * q]), e1 = pexp(x[2 * q + 1]);
         const uint32_t pk = pack2<QT>(e0, e1);
         pb[q] = pk;
         pr = add_pair<QT>(pk, pr);
       }
     }
     l_run = l_run * alpha + pr;
+    // The integral maximum rarely moves once a row has seen its largest keys:
+    // rescale the accumulators only when it moved in some lane of the wave.
+    if (__builtin_amdgcn_ballot_w64(alpha != 1.0f) != 0) {
 #pragma unroll
-    for (int c = 0; c < E; ++c) oacc[c] *= alpha;
+      for (int c = 0; c < E; ++c) oacc[c] *= alpha;
+    }
 #pragma unroll
     for (int c = 0; c < E; ++c)
       oacc[c] = mfma16<QT>(v_operand<QT, FP8, D, FNUZ>(t, c), pb, oacc[c]);
@@ -617,27 +651,31 @@ __global__ __launch_bounds__(64 * kSmallWaves, 2) void small_kernel(Params p) {
     for (int r = 0; r < 4; ++r) sm_o[wave][r16][DQ * g + E * r + c] = oacc[c][r];
   __syncthreads();
 
-  for (int idx = tid; idx < 256; idx += 64 * kSmallWaves) {
+  // Rows x 16 chunks of E values: each thread merges the waves' states of one
+  // (row, chunk) (HW: each wave emits its own rows, four items per lane).
+  constexpr int NW = HW ? 1 : kSmallWaves;
+  const int w0 = HW ? wave : 0;
+  for (int idx = HW ? lane : tid; idx < 256; idx += HW ? 64 : 64 * kSmallWaves) {
     const int row = idx >> 4, chunk = idx & 15;
     const int mrt = row / G, mrh = row - (row / G) * G;
     if (!(row < p.block_q * G && mrt < ntok)) continue;
     const int tok = tok0 + mrt, hh = hbase + mrh;
-    float mw[kSmallWaves];
+    float mw[NW];
     float M = -INFINITY;
 #pragma unroll
-    for (int w = 0; w < kSmallWaves; ++w) {
-      mw[w] = sm_m[w][row];
+    for (int w = 0; w < NW; ++w) {
+      mw[w] = sm_m[w0 + w][row];
       M = fmaxf(M, mw[w]);
     }
     const float sink2 = (!SPLIT && p.sinks != nullptr) ? p.sinks[hh] * kLog2e : -INFINITY;
     const float Mt = fmaxf(M, sink2);
     const float Ms = (Mt == -INFINITY) ? 0.0f : Mt;
     float L = 0.0f;
-    float f[kSmallWaves];
+    float f[NW];
 #pragma unroll
-    for (int w = 0; w < kSmallWaves; ++w) {
+    for (int w = 0; w < NW; ++w) {
       f[w] = fast_exp2(mw[w] - Ms);
-      L += f[w] * sm_l[w][row];
+      L += f[w] * sm_l[w0 + w][row];
     }
     const bool any_key = L > 0.0f;
     float o[E];
@@ -645,7 +683,7 @@ __global__ __launch_bounds__(64 * kSmallWaves, 2) void small_kernel(Params p) {
     for (int e = 0; e < E; ++e) {
       float a = 0.0f;
 #pragma unroll
-      for (int w = 0; w < kSmallWaves; ++w) a += f[w] * sm_o[w][row][E * chunk + e];
+      for (int w = 0; w < NW; ++w) a += f[w] * sm_o[w0 + w][row][E * chunk + e];
       o[e] = a;
     }
     const int64_t rrow = (int64_t)tok * p.num_q_heads + hh;
@@ -684,16 +722,24 @@ template <int QT, bool FP8, int D, bool FNUZ, bool TS>
 hipError_t launch_small_t(const Params& p, bool split, dim3 grid, hipStream_t stream) {
   const bool page16 = (p.block_size % 16) == 0;
   const dim3 block(64 * kSmallWaves);
-  if (split) {
-    if (page16)
-      hipLaunchKernelGGL((small_kernel<QT, FP8, D, true, true, FNUZ, TS>), grid, block, 0, stream, p);
+  if (p.head_waves) {
+    // grid.y counts row blocks; a workgroup takes kSmallWaves of them.
+    if (!page16 || grid.y % kSmallWaves != 0) return hipErrorInvalidValue;
+    const dim3 g4(grid.x, grid.y / kSmallWaves, grid.z);
+    if (split)
+      hipLaunchKernelGGL((small_kernel<QT, FP8, D, true, true, FNUZ, TS, true>), g4, block, 0, stream, p);
     else
-      hipLaunchKernelGGL((small_kernel<QT, FP8, D, true, false, FNUZ, TS>), grid, block, 0, stream, p);
+      hipLaunchKernelGGL((small_kernel<QT, FP8, D, false, true, FNUZ, TS, true>), g4, block, 0, stream, p);
+  } else if (split) {
+    if (page16)
+      hipLaunchKernelGGL((small_kernel<QT, FP8, D, true, true, FNUZ, TS, false>), grid, block, 0, stream, p);
+    else
+      hipLaunchKernelGGL((small_kernel<QT, FP8, D, true, false, FNUZ, TS, false>), grid, block, 0, stream, p);
   } else {
     if (page16)
-      hipLaunchKernelGGL((small_kernel<QT, FP8, D, false, true, FNUZ, TS>), grid, block, 0, stream, p);
+      hipLaunchKernelGGL((small_kernel<QT, FP8, D, false, true, FNUZ, TS, false>), grid, block, 0, stream, p);
     else
-      hipLaunchKernelGGL((small_kernel<QT, FP8, D, false, false, FNUZ, TS>), grid, block, 0, stream, p);
+      hipLaunchKernelGGL((small_kernel<QT, FP8, D, false, false, FNUZ, TS, false>), grid, block, 0, stream, p);
   }
   return hipGetLastError();
 }

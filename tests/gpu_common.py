@@ -78,8 +78,10 @@ def to_device(case, device="cuda"):
 
 
 def run(case, dev=None, path="auto", n_part=0, lse=False, poison_out=True, ws=None,
-        out=None, num_cus=None):
-    """Run one case on the GPU through the C ABI; returns (out fp64 numpy, lse, plan)."""
+        out=None, num_cus=None, plan_edit=None):
+    """Run one case on the GPU through the C ABI; returns (out fp64 numpy, lse, plan).
+    plan_edit: optional function applied to the plan before the launches (the
+    calls of attention.forward, made here so that a test can change the plan)."""
     import paged_varlen_attention_ua_amd.attention as A
     dev = dev or to_device(case)
     q = dev["q"]
@@ -90,6 +92,12 @@ def run(case, dev=None, path="auto", n_part=0, lse=False, poison_out=True, ws=No
     lse_t = None
     if lse:
         lse_t = torch.full(q.shape[:2], float("nan"), dtype=torch.float32, device=q.device)
+    if plan_edit is not None:
+        o, plan = _forward_edited(case, dev, out, lse_t, path, n_part, ws, num_cus, plan_edit)
+        torch.cuda.synchronize()
+        res = o.float().cpu().numpy().astype(np.float64)
+        l = lse_t.cpu().numpy().astype(np.float64) if lse_t is not None else None
+        return res, l, plan
     o, plan = A.forward(q, dev["k_cache"], dev["v_cache"], dev["block_table"],
                         dev["cu_seqlens_q"], dev["seq_lens"],
                         max_seqlen_q=case["max_seqlen_q"], max_seqlen_k=case["max_seqlen_k"],
@@ -107,6 +115,39 @@ def run(case, dev=None, path="auto", n_part=0, lse=False, poison_out=True, ws=No
 
 RECORDS = []
 BAND_MIN = 2.0  # |oracle| from which bf16 outputs get the half-ULP allowance
+
+
+def _forward_edited(case, dev, out, lse_t, path, n_part, ws, num_cus, plan_edit):
+    import ctypes
+    import paged_varlen_attention_ua_amd.attention as A
+    from paged_varlen_attention_ua_amd import binding as B
+    q = dev["q"]
+    prob = A.make_problem(q, dev["k_cache"], dev["v_cache"], dev["block_table"],
+                          num_seqs=len(case["seq_lens"]), max_seqlen_q=case["max_seqlen_q"],
+                          max_seqlen_k=case["max_seqlen_k"], scale=case["scale"],
+                          softcap=case["softcap"], window=case["window"],
+                          k_scale=case["k_scale"], v_scale=case["v_scale"],
+                          alibi_slopes=dev["alibi_slopes"], sinks=dev["sinks"], out=out,
+                          qq_bias=dev.get("qq_bias"), k_token_scales=dev.get("k_token_scales"),
+                          v_token_scales=dev.get("v_token_scales"))
+    path_code = {"auto": B.UA_PATH_AUTO, "2d": B.UA_PATH_2D, "splitkv": B.UA_PATH_SPLITKV}[path]
+    plan = B.ua_plan(prob, num_cus if num_cus is not None else A.device_cus(q.device),
+                     path_code, n_part)
+    plan_edit(plan)
+    args = A.make_args(q, dev["k_cache"], dev["v_cache"], dev["block_table"],
+                       dev["cu_seqlens_q"], dev["seq_lens"], out, lse_t, dev["alibi_slopes"],
+                       dev["sinks"], dev.get("qq_bias"), dev.get("k_token_scales"),
+                       dev.get("v_token_scales"))
+    sp = ctypes.c_void_p(torch.cuda.current_stream(q.device).cuda_stream)
+    if plan.path == B.UA_PATH_2D:
+        B.ua_forward_2d(prob, plan, args, sp)
+    else:
+        if ws is None:
+            ws = torch.empty(max(int(plan.workspace_bytes), 256), dtype=torch.uint8,
+                             device=q.device)
+        B.ua_forward_splitkv(prob, plan, args, ctypes.c_void_p(ws.data_ptr()), ws.numel(), sp)
+        B.ua_reduce(prob, plan, args, ctypes.c_void_p(ws.data_ptr()), ws.numel(), sp)
+    return out, plan
 
 
 def allowed_error(case, ref):

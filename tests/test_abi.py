@@ -72,14 +72,52 @@ def status_of(p, force_path=0, n_part=0):
 
 
 def test_long_decode_splits_to_fill_the_device():
+    # 8 seqs x 8 kv heads = 64 row blocks, a wave each (flag bit 2): 16
+    # workgroups of four per partition, 16 partitions = one workgroup per CU.
     st, plan = status_of(problem())
-    assert st == 0 and plan.path == B.UA_PATH_SPLITKV
-    assert plan.n_part == 4  # 8 seqs x 8 kv heads = 64 groups: one workgroup per CU
-    assert plan.grid_y == 8 and plan.grid_z == 4 and plan.grid_x == 8  # one block per sequence
+    assert st == 0 and plan.path == B.UA_PATH_SPLITKV and plan.flags & 4
+    assert plan.n_part == 16
+    assert plan.grid_y == 8 and plan.grid_z == 16 and plan.grid_x == 8  # one block per sequence
     R = 8 * 32
-    assert plan.workspace_bytes == ((2 * 4 * R * 4 + 255) & ~255) + 4 * R * 128 * 4
+    assert plan.workspace_bytes == ((2 * 16 * R * 4 + 255) & ~255) + 16 * R * 128 * 4
     st, plan = status_of(problem(kv_dtype=B.UA_FP8_E4M3FN, kv_stride_block=16 * 8 * 128))
-    assert st == 0 and plan.n_part == 8
+    assert st == 0 and plan.n_part == 16 and plan.flags & 4
+
+
+def test_wave_per_row_block_needs_four_row_blocks_and_16_slot_halves():
+    # 2 kv heads (2 row blocks): one row block per workgroup, 4 x as many
+    # workgroups per partition, a quarter of the partitions.
+    st, plan = status_of(problem(num_q_heads=16, num_kv_heads=2))
+    assert st == 0 and not plan.flags & 4 and plan.n_part == 16
+    # block size 8: no 16-slot halves
+    st, plan = status_of(problem(block_size=8, kv_stride_block=8 * 8 * 128, num_blocks=8192,
+                                 max_blocks_per_seq=1024))
+    assert st == 0 and not plan.flags & 4 and plan.n_part == 4
+    # MQA decode, 32 query heads over 1 kv head: 2 head groups, 2 row blocks
+    st, plan = status_of(problem(num_kv_heads=1, kv_stride_block=16 * 128,
+                                 kv_stride_slot=128))
+    assert st == 0 and not plan.flags & 4 and plan.grid_y == 2
+    # a full grid (32 sequences of 630 keys) stays one-pass without the flag;
+    # 512 sequences (4096 row blocks = 4 x 4 per CU) take it one-pass
+    st, plan = status_of(problem(num_seqs=32, total_q=32, max_seqlen_k=630))
+    assert st == 0 and plan.n_part == 1 and not plan.flags & 4
+    st, plan = status_of(problem(num_seqs=512, total_q=512, max_seqlen_k=630, num_blocks=1 << 15,
+                                 max_blocks_per_seq=40))
+    assert st == 0 and plan.n_part == 1 and plan.flags & 4
+
+
+def test_wave_per_row_block_flag_is_checked_at_launch():
+    # A plan whose flag bit 2 does not fit the problem is refused before any launch.
+    p = problem(num_q_heads=16, num_kv_heads=2)
+    st, plan = status_of(p)
+    assert st == 0 and not plan.flags & 4
+    plan.flags |= 4
+    args = B.UaArgs()
+    for f in ("q", "k_cache", "v_cache", "block_table", "cu_seqlens_q", "seq_lens", "out"):
+        setattr(args, f, 1 << 20)
+    assert B.lib().ua_forward_splitkv(ctypes.byref(p), ctypes.byref(plan), ctypes.byref(args),
+                                      ctypes.c_void_p(1 << 20), plan.workspace_bytes,
+                                      None) == B.UA_EPLAN
 
 
 def test_few_sequence_decode_splits_to_two_tile_partitions():
@@ -191,12 +229,12 @@ def test_invalid_problems_are_rejected(kw, code):
 def test_fp8_dialects_and_per_token_scales_plan():
     for kvd in (B.UA_FP8_E4M3FN, B.UA_FP8_E4M3FNUZ):
         st, plan = status_of(problem(kv_dtype=kvd, kv_stride_block=16 * 8 * 128))
-        assert st == 0 and plan.n_part == 8
+        assert st == 0 and plan.n_part == 16
         p = problem(kv_dtype=kvd, kv_stride_block=16 * 8 * 128, has_kv_token_scales=1,
                     ks_stride_block=8 * 16, ks_stride_slot=1, ks_stride_head=16,
                     vs_stride_block=16 * 8, vs_stride_slot=8, vs_stride_head=1)
         st, plan2 = status_of(p)
-        assert st == 0 and plan2.n_part == 8
+        assert st == 0 and plan2.n_part == 16
         assert plan2.problem_hash != plan.problem_hash
         # per-token arrays missing from the call
         args = B.UaArgs()

@@ -382,6 +382,78 @@ def test_split_partition_counts_agree(name):
                                         f"differ by more than one ULP (max {diff.max():.3e})"
 
 
+# Decode shapes with a multiple of four row blocks (kv heads x head groups),
+# where the planner gives each wave its own row block: head dims 64 and 256,
+# four-token query blocks, fp8 with per-token scales and a softcap, and 64 query
+# heads over 2 kv heads (two head groups of 32 each -> 4 row blocks).
+WAVE_ROW_CASES = {
+    "d64_bf16_32q8kv_bs32_sinks": dict(
+        seqs=None, num_seqs=6, q_len=1, kv_range=(2500, 3100), head_dim=64, num_q_heads=32,
+        num_kv_heads=8, block_size=32, q_dtype="bf16", sinks=True, seed=301),
+    "d256_fp16_16q4kv_alibi": dict(
+        seqs=None, num_seqs=4, q_len=1, kv_range=(1800, 2200), head_dim=256, num_q_heads=16,
+        num_kv_heads=4, block_size=16, q_dtype="f16", alibi=True, seed=302),
+    "q4_bf16_32q8kv_window2000": dict(
+        seqs=None, num_seqs=8, q_len=4, kv_range=(3000, 3500), head_dim=128, num_q_heads=32,
+        num_kv_heads=8, block_size=16, q_dtype="bf16", window=2000, seed=303),
+    "fnuz_pertoken_softcap": dict(
+        seqs=None, num_seqs=4, q_len=1, kv_range=(2000, 2600), head_dim=128, num_q_heads=32,
+        num_kv_heads=8, block_size=32, q_dtype="bf16", kv_dtype="e4m3fnuz", o_dtype="bf16",
+        token_scales=True, softcap=30.0, seed=304),
+    "e4m3fn_64q2kv": dict(
+        seqs=None, num_seqs=8, q_len=1, kv_range=(1400, 1700), head_dim=128, num_q_heads=64,
+        num_kv_heads=2, block_size=16, q_dtype="bf16", kv_dtype="e4m3fn", o_dtype="bf16",
+        seed=305),
+}
+
+
+@functools.lru_cache(maxsize=2)
+def _wave_row_case(name):
+    case = make_case(**WAVE_ROW_CASES[name])
+    ref, lse = oracle.attention(**case)
+    return case, ref, lse, to_device(case)
+
+
+def _set_flag4(plan):
+    plan.flags |= 4
+
+
+def _clear_flag4(plan):
+    plan.flags &= ~4
+
+
+@pytest.mark.parametrize("name", list(WAVE_ROW_CASES))
+def test_wave_per_row_block_matches_shared_row_block(name):
+    """A wave per row block (plan flag bit 2) and four waves per row block give
+    results within tolerance of the oracle and within one output ULP of each
+    other, one-pass and split; the planner picks the former for these shapes."""
+    case, ref, ref_lse, dev = _wave_row_case(name)
+    outs = {}
+    got, lse, plan = run(case, dev, lse=True)
+    assert plan.kernel == 0 and plan.flags & 4 and plan.n_part > 1
+    compare(case, got, ref, label=f"{name}/auto-wave")
+    check_lse(lse, ref_lse, case=case, label=f"{name}/auto-wave")
+    outs["auto-wave"] = got
+    for label, path, n, edit in (("auto-shared", "auto", 0, _clear_flag4),
+                                 ("split5-wave", "splitkv", 5, _set_flag4),
+                                 ("split5-shared", "splitkv", 5, _clear_flag4),
+                                 ("2d-wave", "2d", 0, _set_flag4),
+                                 ("2d-shared", "2d", 0, _clear_flag4)):
+        got, lse, plan = run(case, dev, path=path, n_part=n, lse=True, plan_edit=edit)
+        assert bool(plan.flags & 4) == (edit is _set_flag4)
+        compare(case, got, ref, label=f"{name}/{label}")
+        check_lse(lse, ref_lse, case=case, label=f"{name}/{label}")
+        outs[label] = got
+    keys = list(outs)
+    for i, a in enumerate(keys):
+        for b in keys[i + 1:]:
+            x, y = outs[a], outs[b]
+            diff = np.abs(x - y)
+            one = ulp(np.maximum(np.maximum(np.abs(x), np.abs(y)), 1e-3), case["o_dtype"])
+            assert (diff <= one).all(), f"{a} vs {b}: {int((diff > one).sum())} elements " \
+                                        f"differ by more than one ULP (max {diff.max():.3e})"
+
+
 def test_nan_workspace_not_read():
     case, ref, _ = _workload("fp8kv_decode_b8_ctx6700_w4096")
     dev = _dev("fp8kv_decode_b8_ctx6700_w4096")
