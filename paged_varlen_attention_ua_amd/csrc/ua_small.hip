@@ -38,6 +38,8 @@
 //     raw dot product, the V scale the probability fed to the PV MFMA (the
 //     softmax sum keeps the unscaled probability).
 
+#include <type_traits>
+
 #include "ua_device.h"
 
 namespace ua {
@@ -392,6 +394,11 @@ __global__ __launch_bounds__(64 * kSmallWaves, 2) void small_kernel(Params p) {
   const int pos = p0 + rt;
   const int row_lo = p.window > 0 ? max(kl, pos - p.window + 1) : kl;
   const int row_hi = min(k1, pos + 1);
+  // Keys every row of the block sees, [vis_lo, vis_hi): the window start of
+  // its last token and the causal end of its first.  Tiles inside it need no
+  // per-key mask.
+  const int vis_lo = p.window > 0 ? max(kl, p0 + ntok - p.window) : kl;
+  const int vis_hi = min(k1, p0 + 1);
   const float slope2 = (p.alibi != nullptr && row_ok) ? p.alibi[h] * kLog2e : 0.0f;
 
   // Q as the B operand of S^T = K Q^T (same head-dim map as K).
@@ -499,16 +506,32 @@ __global__ __launch_bounds__(64 * kSmallWaves, 2) void small_kernel(Params p) {
 #pragma unroll
       for (int j = 0; j < 8; ++j) ksc[j] = lane_get(t.sc, 16 * g + j);
     }
+    // Logits in base-2 units; the feature tests are uniform, one branch each.
     float x[8];
 #pragma unroll
     for (int hb = 0; hb < 2; ++hb) {
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        const int key = kt + 16 * hb + 4 * r + g;
         float raw = sacc[hb][r];
         if constexpr (tsc) raw *= ksc[4 * hb + r];
-        float v = p.softcap_on ? p.cap_out2 * tanh_fast(raw * p.cap_in) : raw * p.qk_scale2;
-        x[4 * hb + r] = v + slope2 * (float)(key - ctx);
+        x[4 * hb + r] = raw;
+      }
+    }
+    if (p.softcap_on) {
+#pragma unroll
+      for (int j = 0; j < 8; ++j) x[j] = p.cap_out2 * tanh_fast(x[j] * p.cap_in);
+    } else {
+#pragma unroll
+      for (int j = 0; j < 8; ++j) x[j] *= p.qk_scale2;
+    }
+    if (p.alibi != nullptr) {
+#pragma unroll
+      for (int hb = 0; hb < 2; ++hb) {
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int key = kt + 16 * hb + 4 * r + g;
+          x[4 * hb + r] = x[4 * hb + r] + slope2 * (float)(key - ctx);
+        }
       }
     }
     // QQ-bias qq[i][key - ctx] (i = this row's index in its chunk) on the
@@ -524,15 +547,21 @@ __global__ __launch_bounds__(64 * kSmallWaves, 2) void small_kernel(Params p) {
           x[4 * hb + r] = __builtin_fmaf(b, kLog2e, x[4 * hb + r]);
         }
     }
+    const bool full = kt >= vis_lo && kt + kSmallTile <= vis_hi;  // uniform
     float mt = -INFINITY;
+    if (full) {
 #pragma unroll
-    for (int hb = 0; hb < 2; ++hb) {
+      for (int j = 0; j < 8; ++j) mt = fmaxf(mt, x[j]);
+    } else {
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int key = kt + 16 * hb + 4 * r + g;
-        const bool vis = key >= row_lo && key < row_hi;
-        x[4 * hb + r] = vis ? x[4 * hb + r] : -INFINITY;
-        mt = fmaxf(mt, x[4 * hb + r]);
+      for (int hb = 0; hb < 2; ++hb) {
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int key = kt + 16 * hb + 4 * r + g;
+          const bool vis = key >= row_lo && key < row_hi;
+          x[4 * hb + r] = vis ? x[4 * hb + r] : -INFINITY;
+          mt = fmaxf(mt, x[4 * hb + r]);
+        }
       }
     }
     mt = wave_max_xor(mt, 16);
@@ -543,35 +572,42 @@ __global__ __launch_bounds__(64 * kSmallWaves, 2) void small_kernel(Params p) {
     m_run = m_new;
     // p = 2^(x - m) as 2^(x - rint(x)) scaled by 2^(rint(x) - m) (ldexp, exact):
     // x - rint(x) is exact for every float while x - m is not (|x| < 1 < m), so
-    // p's mantissa depends on x alone, never on the running maximum.  Masked
-    // keys (-inf) and keys more than 200 below m give 0.
+    // p's mantissa depends on x alone, never on the running maximum.  Keys more
+    // than 200 below m give 0, and so do masked keys (-inf), clamped to that
+    // floor first (tiles without masked keys skip the clamp).
     const float x_lo = m_use - 200.0f;
-    auto pexp = [&](float xv) __attribute__((always_inline)) {
-      const float xc = fmaxf(xv, x_lo);
-      const float kx = __builtin_rintf(xc);
-      return __builtin_amdgcn_ldexpf(fast_exp2(xc - kx), (int)(kx - m_use));
-    };
     u32x4 pb;
     float pr = 0.0f;
-    if constexpr (tsc) {
-      // The PV weights carry the V scales (from lanes 16 g + 8 + 4 hb + r); the
-      // softmax sum does not.
+    auto form_p = [&](auto clamp) __attribute__((always_inline)) {
+      auto pexp = [&](float xv) __attribute__((always_inline)) {
+        const float xc = decltype(clamp)::value ? fmaxf(xv, x_lo) : xv;
+        const float kx = __builtin_rintf(xc);
+        return __builtin_amdgcn_ldexpf(fast_exp2(xc - kx), (int)(kx - m_use));
+      };
+      if constexpr (tsc) {
+        // The PV weights carry the V scales (from lanes 16 g + 8 + 4 hb + r);
+        // the softmax sum does not.
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const float e0 = pexp(x[2 * q]), e1 = pexp(x[2 * q + 1]);
-        pb[q] = pack2<QT>(e0 * lane_get(t.sc, 16 * g + 8 + 2 * q),
-                          e1 * lane_get(t.sc, 16 * g + 9 + 2 * q));
-        pr += e0 + e1;
-      }
-    } else {
+        for (int q = 0; q < 4; ++q) {
+          const float e0 = pexp(x[2 * q]), e1 = pexp(x[2 * q + 1]);
+          pb[q] = pack2<QT>(e0 * lane_get(t.sc, 16 * g + 8 + 2 * q),
+                            e1 * lane_get(t.sc, 16 * g + 9 + 2 * q));
+          pr += e0 + e1;
+        }
+      } else {
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const float e0 = pexp(x[2 * q]), e1 = pexp(x[2 * q + 1]);
-        const uint32_t pk = pack2<QT>(e0, e1);
-        pb[q] = pk;
-        pr = add_pair<QT>(pk, pr);
+        for (int q = 0; q < 4; ++q) {
+          const float e0 = pexp(x[2 * q]), e1 = pexp(x[2 * q + 1]);
+          const uint32_t pk = pack2<QT>(e0, e1);
+          pb[q] = pk;
+          pr = add_pair<QT>(pk, pr);
+        }
       }
-    }
+    };
+    if (full)
+      form_p(std::false_type{});
+    else
+      form_p(std::true_type{});
     l_run = l_run * alpha + pr;
     // The integral maximum rarely moves once a row has seen its largest keys:
     // rescale the accumulators only when it moved in some lane of the wave.
