@@ -280,6 +280,22 @@ __device__ __forceinline__ u32x4 v_operand(const Tile<QT, FP8, D>& t, int c) {
   return op;
 }
 
+// fp8 caches: the A operands of PV MFMAs c and c + 1 (c even) together.  One
+// byte permute gathers byte c of keys 2q and 2q+1 into the low half and byte
+// c + 1 into the high half; the two halves convert to the two operands.
+template <int QT, int D, bool FNUZ>
+__device__ __forceinline__ void v_operand_pair(const Tile<QT, true, D>& t, int c, u32x4& op0,
+                                               u32x4& op1) {
+  const uint32_t bc = c & 3;
+  const uint32_t sel = bc | ((bc + 4) << 8) | ((bc + 1) << 16) | ((bc + 5) << 24);
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const uint32_t w = perm_b32(t.v[2 * q + 1][c >> 2], t.v[2 * q][c >> 2], sel);
+    op0[q] = fp8x2_to<QT, FNUZ>(w, false);
+    op1[q] = fp8x2_to<QT, FNUZ>(w, true);
+  }
+}
+
 // Float handed from lane src to this lane (ds_bpermute; byte address 4 src).
 __device__ __forceinline__ float lane_get(float v, int src) {
   return __builtin_bit_cast(float, __builtin_amdgcn_ds_bpermute(4 * src, __builtin_bit_cast(int, v)));
@@ -615,9 +631,19 @@ __global__ __launch_bounds__(64 * kSmallWaves, 2) void small_kernel(Params p) {
 #pragma unroll
       for (int c = 0; c < E; ++c) oacc[c] *= alpha;
     }
+    if constexpr (FP8 && E % 2 == 0) {
 #pragma unroll
-    for (int c = 0; c < E; ++c)
-      oacc[c] = mfma16<QT>(v_operand<QT, FP8, D, FNUZ>(t, c), pb, oacc[c]);
+      for (int c = 0; c < E; c += 2) {
+        u32x4 op0, op1;
+        v_operand_pair<QT, D, FNUZ>(t, c, op0, op1);
+        oacc[c] = mfma16<QT>(op0, pb, oacc[c]);
+        oacc[c + 1] = mfma16<QT>(op1, pb, oacc[c + 1]);
+      }
+    } else {
+#pragma unroll
+      for (int c = 0; c < E; ++c)
+        oacc[c] = mfma16<QT>(v_operand<QT, FP8, D, FNUZ>(t, c), pb, oacc[c]);
+    }
   };
 
   // Tile loop.  Paged caches with D <= 128 keep two tiles in flight per wave
