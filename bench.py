@@ -362,24 +362,26 @@ def blas_threads():
         return os.cpu_count() or 1
 
 
-class SclkSampler:
-    """Current graphics clock (MHz) read from the driver on a host thread every
-    few milliseconds while the GPU runs a sustained load: amdsmi's GFX clock,
-    else the starred level of sysfs pp_dpm_sclk.  Read-only driver queries."""
+class ClockSampler:
+    """Current graphics (kind "GFX") or memory ("MEM") clock in MHz, read from
+    the driver on a host thread every few milliseconds while the GPU runs a
+    sustained load: amdsmi's clock info, else the starred level of sysfs
+    pp_dpm_sclk / pp_dpm_mclk.  Read-only driver queries."""
 
-    def __init__(self):
+    def __init__(self, kind="GFX"):
         self.samples, self.source, self._read = [], None, None
         try:
             import amdsmi
             amdsmi.amdsmi_init()
             h = amdsmi.amdsmi_get_processor_handles()[0]
-            amdsmi.amdsmi_get_clock_info(h, amdsmi.AmdSmiClkType.GFX)
-            self._read = lambda: float(
-                amdsmi.amdsmi_get_clock_info(h, amdsmi.AmdSmiClkType.GFX)["clk"])
-            self.source = "amdsmi GFX clock"
+            clk = getattr(amdsmi.AmdSmiClkType, kind)
+            amdsmi.amdsmi_get_clock_info(h, clk)
+            self._read = lambda: float(amdsmi.amdsmi_get_clock_info(h, clk)["clk"])
+            self.source = f"amdsmi {kind} clock"
         except Exception:
             import glob
-            files = sorted(glob.glob("/sys/class/drm/card*/device/pp_dpm_sclk"))
+            files = sorted(glob.glob("/sys/class/drm/card*/device/pp_dpm_" +
+                                     ("sclk" if kind == "GFX" else "mclk")))
             if files:
                 def rd(f=files[0]):
                     for line in open(f):
@@ -389,7 +391,7 @@ class SclkSampler:
                     return None
                 try:
                     rd()
-                    self._read, self.source = rd, "sysfs pp_dpm_sclk"
+                    self._read, self.source = rd, "sysfs " + os.path.basename(files[0])
                 except Exception:
                     pass
 
@@ -440,7 +442,7 @@ def prefill_roofline(case, steps, warmup, name):
     r = Runner(case, to_device(case))
     sp = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
     n = max(8, int(1.0 / max(rr["kernel_ms"] * 1e-3, 1e-5)))
-    sampler = SclkSampler()
+    sampler = ClockSampler("GFX")
 
     def load():
         for _ in range(n):
@@ -466,6 +468,34 @@ def prefill_roofline(case, steps, warmup, name):
         rec["peak_at_sclk"] = round(pk, 1)
         rec["frac_at_sclk"] = round(kt / pk, 4)
     return rec
+
+
+def memory_clock_under_load(case, seconds=0.5):
+    """Median memory clock (MHz) sampled while the workload's main kernel runs
+    back to back for about `seconds`, and the clock's source; None without a
+    readable clock."""
+    import torch
+    from tests.gpu_common import to_device
+    r = Runner(case, to_device(case))
+    sp = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    sampler = ClockSampler("MEM")
+    if sampler.source is None:
+        return None
+    n = 8
+    t0 = time.time()
+    for _ in range(n):
+        r.step_main(sp)
+    torch.cuda.synchronize()
+    per = max((time.time() - t0) / n, 1e-6)
+    n = max(8, int(seconds / per))
+
+    def load():
+        for _ in range(n):
+            r.step_main(sp)
+        torch.cuda.synchronize()
+    sampler.run(load)
+    mhz = sampler.median()
+    return (mhz, sampler.source) if mhz else None
 
 
 def prefill_cpu_baseline(case, budget_s=8.0, chunk=32, seed=5):
@@ -551,6 +581,7 @@ def main():
     warm = None if args.quick else time_case(head, args.steps, args.warmup,
                                              kernel_events=False, rotate=False)
     traffic = traffic_entry()
+    mclk = None if args.quick else memory_clock_under_load(head)
     line = {
         "metric": METRIC, "value": round(gbs, 2), "unit": "GB/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(r["ms_per_step"], 5),
@@ -579,7 +610,9 @@ def main():
                      if traffic is not None else "counters not taken on these sources",
                      "kernel": "small_kernel (split-KV partitions)" if r["path"] == 2
                      else "small_kernel (one pass)",
-                     "kernel_ms": round(r["kernel_ms"], 5)},
+                     "kernel_ms": round(r["kernel_ms"], 5),
+                     "mclk_under_load_mhz": mclk[0] if mclk else None,
+                     "mclk_source": mclk[1] if mclk else None},
     }
     if not args.quick:
         others = {}
