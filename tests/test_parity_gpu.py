@@ -384,8 +384,10 @@ def test_split_partition_counts_agree(name):
 
 # Decode shapes with a multiple of four row blocks (kv heads x head groups),
 # where the planner gives each wave its own row block: head dims 64 and 256,
-# four-token query blocks, fp8 with per-token scales and a softcap, and 64 query
-# heads over 2 kv heads (two head groups of 32 each -> 4 row blocks).
+# four-token query blocks (with a window; with a QQ-bias), fp8 with per-token
+# scales and a softcap, 64 query heads over 2 kv heads (two head groups of 32
+# each -> 4 row blocks), and a batch whose row blocks fill the device four
+# times over (planned one-pass).
 WAVE_ROW_CASES = {
     "d64_bf16_32q8kv_bs32_sinks": dict(
         seqs=None, num_seqs=6, q_len=1, kv_range=(2500, 3100), head_dim=64, num_q_heads=32,
@@ -404,6 +406,13 @@ WAVE_ROW_CASES = {
         seqs=None, num_seqs=8, q_len=1, kv_range=(1400, 1700), head_dim=128, num_q_heads=64,
         num_kv_heads=2, block_size=16, q_dtype="bf16", kv_dtype="e4m3fn", o_dtype="bf16",
         seed=305),
+    "q4_qqbias_bf16_32q8kv": dict(
+        seqs=None, num_seqs=8, q_len=4, kv_range=(2000, 2600), head_dim=128, num_q_heads=32,
+        num_kv_heads=8, block_size=16, q_dtype="bf16", qq_bias=True, seed=306),
+    # 160 sequences x 8 kv heads = 1280 row blocks, over four per CU: one pass
+    "b160_onepass_bf16_32q8kv": dict(
+        seqs=None, num_seqs=160, q_len=1, kv_range=(300, 500), head_dim=128, num_q_heads=32,
+        num_kv_heads=8, block_size=16, q_dtype="bf16", seed=307),
 }
 
 
@@ -430,7 +439,7 @@ def test_wave_per_row_block_matches_shared_row_block(name):
     case, ref, ref_lse, dev = _wave_row_case(name)
     outs = {}
     got, lse, plan = run(case, dev, lse=True)
-    assert plan.kernel == 0 and plan.flags & 4 and plan.n_part > 1
+    assert plan.kernel == 0 and plan.flags & 4
     compare(case, got, ref, label=f"{name}/auto-wave")
     check_lse(lse, ref_lse, case=case, label=f"{name}/auto-wave")
     outs["auto-wave"] = got
