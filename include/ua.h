@@ -196,7 +196,9 @@ ua_status ua_forward_2d(const ua_problem* prob, const ua_plan_t* plan, const ua_
  *   m[p][r]   the base-2 reference the partition's weights are taken against:
  *             within 8 of the largest base-2 logit (x * log2 e) over the
  *             partition's visible keys (small query blocks, plan->kernel 0:
- *             that largest logit rounded up to an integer),
+ *             that largest logit rounded up to an integer; large query blocks
+ *             at head dim 256: at most 64 below it for bf16 queries, 15 for
+ *             fp16, never above it),
  *   l[p][r]   sum of the weights w = 2^(x*log2e - m) over those keys (0: the
  *             partition saw nothing),
  *   acc[p][r][D]  sum of w * v (v without v_scale),

@@ -57,6 +57,19 @@ __device__ __forceinline__ uint32_t pack2(float a, float b) {
   }
 }
 
+// acc + lo + hi of a packed pair of QT values (one v_dot2c against (1, 1)):
+// the sum of p values exactly as rounded for the PV MFMA.
+template <int QT>
+__device__ __forceinline__ float add_pair(uint32_t pk, float acc) {
+  if constexpr (QT == UA_F16) {
+    return __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, pk),
+                                  __builtin_bit_cast(f16x2, 0x3c003c00u), acc, false);
+  } else {
+    return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, pk),
+                                           __builtin_bit_cast(bf16x2, 0x3f803f80u), acc, false);
+  }
+}
+
 // Byte permute: result byte i = byte sel_i of the 8-byte value {hi:lo}.
 __device__ __forceinline__ uint32_t perm_b32(uint32_t hi, uint32_t lo, uint32_t sel) {
   return __builtin_amdgcn_perm(hi, lo, sel);

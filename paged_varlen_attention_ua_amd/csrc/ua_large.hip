@@ -22,8 +22,11 @@
 //     feeds exp2), with the running maximum only moved when a tile's maximum
 //     exceeds it by more than 8 (exact up to rounding: every key of a row is
 //     scaled by the same maximum between moves, and p <= 2^8 stays
-//     representable); p is formed against the running maximum first and the
-//     tile maximum is only taken when a lane's sum of p exceeds 2^8;
+//     representable); eight-wave groups form p against the running maximum
+//     first and take the tile maximum only when a lane's sum of p exceeds
+//     2^8; head dim 256 instead holds each row's first maximum and runs the
+//     tiles again from the largest one in the rare case a later tile exceeds
+//     it by more than the P type can carry;
 //   * causal, window and range masks are applied only on tiles that need them
 //     (the mask-phase split of the README's "BLOCK_M=128" section);
 //   * O^T = V^T P^T on 32x32x16 MFMA: P^T is already the B operand in the
@@ -322,6 +325,21 @@ __global__ __launch_bounds__(64 * NW, (large_min_groups<D, NW, FP8 && TS>())) vo
 #pragma unroll
   for (int d = 0; d < C::DB; ++d) oacc[d] = f32x16{};
   float m_run = -INFINITY, l_run = 0.0f;
+  // Head dim 256 in four-wave groups keeps O in AGPRs, where any rescale of it
+  // inside the tile loop (however written) made the compiler copy all 128
+  // accumulators to VGPRs on every tile (measured on MI355X: the 8k prompt at
+  // D = 256 ran at 670 TFLOP/s with the copies, 800 without).  So the running
+  // maximum is held: a row's first visible tile sets it (O and l are still
+  // zero then) and p = 2^(x - m) stays at or below 2^kHoldSpan unless a later
+  // tile's maximum exceeds it by more than that; then the workgroup runs its
+  // tiles a second time from each row's largest maximum (m_seen), which no tile
+  // can exceed.  l is then the sum of p as rounded for the PV MFMA (see below).
+  // The span keeps p finite in the P type: 2^15 < 65504, the largest finite
+  // fp16 value; bf16 has the exponent range of fp32.
+  constexpr bool kHold = D > 128 && NW == 4;
+  constexpr float kHoldSpan = QT == UA_F16 ? 15.0f : 64.0f;
+  float m_seen = -INFINITY;
+  bool redo = false;
   const float c2 = p.qk_scale2;
 
   // Stage the block-table entries of the workgroup's key range [kl, k1).
@@ -703,14 +721,23 @@ __global__ __launch_bounds__(64 * NW, (large_min_groups<D, NW, FP8 && TS>())) vo
 #pragma unroll
         for (int r = 0; r < 16; ++r) mt = fmaxf(mt, sacc[kb][r]);
       mt = wave_max_xor(mt, 32) * cs;
-      const bool need = mt > m_run + 8.0f;
-      if (__builtin_amdgcn_ballot_w64(need)) {
-        const float m_new = need ? mt : m_run;
-        const float alpha = need ? fast_exp2(m_run - m_new) : 1.0f;  // m_run = -inf -> 0
-        l_run *= alpha;
+      if constexpr (kHold) {
+        // Branch-free: a branch here splits the scheduling region of the PV
+        // loop below, which then loses its V-read lead.
+        m_seen = fmaxf(m_seen, mt);
+        const bool first = m_run == -INFINITY;  // O and l are still zero
+        redo = redo || (!first && mt > m_run + kHoldSpan);
+        m_run = first ? mt : m_run;
+      } else {
+        const bool need = mt > m_run + 8.0f;
+        if (__builtin_amdgcn_ballot_w64(need)) {
+          const float m_new = need ? mt : m_run;
+          const float alpha = need ? fast_exp2(m_run - m_new) : 1.0f;  // m_run = -inf -> 0
+          l_run *= alpha;
 #pragma unroll
-        for (int d = 0; d < C::DB; ++d) oacc[d] *= alpha;
-        m_run = m_new;
+          for (int d = 0; d < C::DB; ++d) oacc[d] *= alpha;
+          m_run = m_new;
+        }
       }
       const float m_use = (m_run == -INFINITY) ? 0.0f : m_run;
       psum = 0.0f;
@@ -727,11 +754,19 @@ __global__ __launch_bounds__(64 * NW, (large_min_groups<D, NW, FP8 && TS>())) vo
               fast_exp2(__builtin_fmaf(sacc[kk >> 1][8 * (kk & 1) + 2 * q], cs, -m_use));
           const float b =
               fast_exp2(__builtin_fmaf(sacc[kk >> 1][8 * (kk & 1) + 2 * q + 1], cs, -m_use));
-          psum += a + b;
-          if constexpr (tsc)
+          if constexpr (tsc) {
+            psum += a + b;
             pop[kk][q] = pack2<QT>(a * v4[q >> 1][2 * (q & 1)], b * v4[q >> 1][2 * (q & 1) + 1]);
-          else
+          } else if constexpr (kHold) {
+            // Normalise by the sum of p as rounded for the PV MFMA: with a held
+            // maximum the dominant keys' p are far from 1, and dividing their
+            // rounded weights by an unrounded sum would cost up to 2^-9 of O.
             pop[kk][q] = pack2<QT>(a, b);
+            psum = add_pair<QT>(pop[kk][q], psum);
+          } else {
+            psum += a + b;
+            pop[kk][q] = pack2<QT>(a, b);
+          }
         }
       }
     }
@@ -791,6 +826,8 @@ __global__ __launch_bounds__(64 * NW, (large_min_groups<D, NW, FP8 && TS>())) vo
   // Copy instructions one wave issues per tile (K and V).
   constexpr int CPW = 2 * C::BPW;
 
+  __shared__ int sRedo[NW];
+  for (int pass = 0; pass < (kHold ? 2 : 1); ++pass) {
   // Prologue: tables (and scales) of tiles 0 .. NBUF - 1, one wave each; then
   // tiles 0 .. NBUF - 2 are copied (fp8: tile 0 staged) and tile 0 waited for.
   if (wave < NBUF && wave < ntiles) {
@@ -947,6 +984,23 @@ __global__ __launch_bounds__(64 * NW, (large_min_groups<D, NW, FP8 && TS>())) vo
       }
     }
   }
+  if constexpr (kHold) {
+    // Second pass when any row of the workgroup exceeded its held maximum.
+    const bool wr = __builtin_amdgcn_ballot_w64(redo) != 0;
+    if (lane == 0) sRedo[wave] = wr ? 1 : 0;
+    __syncthreads();
+    bool any = false;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) any = any || sRedo[w] != 0;
+    __syncthreads();
+    if (!any || pass > 0) break;
+#pragma unroll
+    for (int d = 0; d < C::DB; ++d) oacc[d] = f32x16{};
+    l_run = 0.0f;
+    m_run = m_seen;
+    redo = false;
+  }
+  }  // pass
 
   if (!row_ok) return;
   // Lanes l and l ^ 32 hold the same row: total l.

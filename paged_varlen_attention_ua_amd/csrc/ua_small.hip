@@ -61,19 +61,6 @@ namespace {
 // most ln(1 + 2^-8) for bf16 and ln(1 + 2^-11) for fp16.
 __device__ __forceinline__ float integral_max(float m) { return __builtin_ceilf(m); }
 
-// acc + lo + hi of a packed pair of QT values (one v_dot2c against (1, 1)):
-// the sum of p values exactly as rounded for the PV MFMA.
-template <int QT>
-__device__ __forceinline__ float add_pair(uint32_t pk, float acc) {
-  if constexpr (QT == UA_F16) {
-    return __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, pk),
-                                  __builtin_bit_cast(f16x2, 0x3c003c00u), acc, false);
-  } else {
-    return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, pk),
-                                           __builtin_bit_cast(bf16x2, 0x3f803f80u), acc, false);
-  }
-}
-
 // Load N dwords (N in {1, 2, 4, 8}) from a 4*N-byte aligned address.
 template <int N>
 __device__ __forceinline__ void load_dw(const char* ptr, uint32_t* dst) {

@@ -463,6 +463,42 @@ def test_wave_per_row_block_matches_shared_row_block(name):
                                         f"differ by more than one ULP (max {diff.max():.3e})"
 
 
+@pytest.mark.parametrize("factor", [8.0, 1.5])
+@pytest.mark.parametrize("q_dtype", ["bf16", "f16"])
+def test_d256_held_maximum_second_pass(q_dtype, factor):
+    """Head dim 256 (four-wave groups hold each row's running maximum instead
+    of rescaling O, and run the tiles again when a later tile exceeds it by
+    more than 64 in base 2 for bf16, 15 for fp16).  One key is made `factor`
+    x a query row: 8x scores ~128 natural units (~185 in base 2) above the
+    row's first tile, past both spans, so its workgroup runs a second pass;
+    1.5x scores ~24 (~35 in base 2), which bf16 carries in one pass (p up to
+    2^35) and fp16 cannot (65504 < 2^16), so only fp16 runs the second pass.
+    Every row, that one included, matches the oracle, one-pass and split."""
+    case = make_case(seqs=[(200, 600)], head_dim=256, num_q_heads=8, num_kv_heads=2,
+                     block_size=16, q_dtype=q_dtype, seed=401)
+    q_bits = case["q"]
+    k_bits = case["k_cache"]
+    if q_dtype == "bf16":  # bf16 bits -> float32 and back (truncating; the
+        # oracle reads the stored bits either way)
+        qf = (q_bits[150, 0].astype(np.uint32) << 16).view(np.float32)
+        kf = (np.float32(factor) * qf).astype(np.float32)
+        kb = (kf.view(np.uint32) >> 16).astype(np.uint16)
+    else:
+        qf = q_bits[150, 0].view(np.float16).astype(np.float32)
+        kb = (np.float32(factor) * qf).astype(np.float16).view(np.uint16)
+    key = 500  # visible to query tokens 100.. (context 400)
+    blk = int(case["block_table"][0][key // 16])
+    k_bits[blk, key % 16, 0] = kb
+    ref, ref_lse = oracle.attention(**case)
+    dev = to_device(case)
+    for path, n in (("auto", 0), ("2d", 0), ("splitkv", 3)):
+        got, lse, plan = run(case, dev, path=path, n_part=n, lse=True)
+        assert plan.kernel == 1
+        label = f"d256-hold{factor:g}/{path}{n}"
+        compare(case, got, ref, label=label)
+        check_lse(lse, ref_lse, case=case, label=label)
+
+
 def test_nan_workspace_not_read():
     case, ref, _ = _workload("fp8kv_decode_b8_ctx6700_w4096")
     dev = _dev("fp8kv_decode_b8_ctx6700_w4096")
