@@ -159,6 +159,20 @@ def clone_dev(dev):
     return {k: (v.clone() if v is not None else None) for k, v in dev.items()}
 
 
+WARM_S = 0.25
+
+
+def warm_graph(g, n_min):
+    """Replay g (untimed) at least n_min times and for at least WARM_S seconds."""
+    import torch
+    t_end = time.perf_counter() + WARM_S
+    n = 0
+    while n < n_min or time.perf_counter() < t_end:
+        g.replay()
+        torch.cuda.synchronize()
+        n += 1
+
+
 def time_case(case, steps, warmup, path="auto", n_part=0, touched=None, kernel_events=True,
               graph=True, rotate=True):
     """Time one workload over R rotated input copies (R = 1 with rotate=False:
@@ -169,7 +183,12 @@ def time_case(case, steps, warmup, path="auto", n_part=0, touched=None, kernel_e
     and replayed, so the per-step time is the GPU's, not the Python launcher's
     (ms_per_step).  Kernel pass: R launches of the main kernel alone (one-pass
     or partition kernel, no reduce) captured and replayed the same way, timed
-    with HIP events on the replay stream (kernel_ms).
+    with HIP events on the replay stream (kernel_ms).  Each graph is replayed,
+    untimed, for at least WARM_S seconds first: after the host-side input
+    generation the GPU has idled and its clock ramps back up over tens of
+    milliseconds, so a short first timing ran partly at the lower clock (seen
+    as a one-pass prefill step 7-10% slower than its own kernel alone, which
+    launches the same kernel).
     """
     import torch
     from tests.gpu_common import to_device
@@ -209,9 +228,7 @@ def time_case(case, steps, warmup, path="auto", n_part=0, touched=None, kernel_e
             cap = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
             for r in runners:
                 r.step(cap)
-        for _ in range(max(1, warmup // R)):
-            g.replay()
-        torch.cuda.synchronize()
+        warm_graph(g, max(1, warmup // R))
         reps = max(1, math.ceil(steps / R))
         t0.record()
         for _ in range(reps):
@@ -225,8 +242,7 @@ def time_case(case, steps, warmup, path="auto", n_part=0, touched=None, kernel_e
                 cap = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
                 for r in runners:
                     r.step_main(cap)
-            gk.replay()
-            torch.cuda.synchronize()
+            warm_graph(gk, 1)
             t0.record()
             for _ in range(reps):
                 gk.replay()
