@@ -6,6 +6,7 @@ so any read of them or any unwritten output shows up as a failure.
 """
 
 import ctypes
+import math
 import functools
 
 import numpy as np
@@ -495,6 +496,47 @@ def test_d256_held_maximum_second_pass(q_dtype, factor):
         got, lse, plan = run(case, dev, path=path, n_part=n, lse=True)
         assert plan.kernel == 1
         label = f"d256-hold{factor:g}/{path}{n}"
+        compare(case, got, ref, label=label)
+        check_lse(lse, ref_lse, case=case, label=label)
+
+
+@pytest.mark.parametrize("token_scale_mult", [None, 1.0, 4.0])
+def test_d256_held_maximum_fp8_cache(token_scale_mult):
+    """The held maximum of the head-dim-256 prefill kernel with fp8 caches
+    (staged through registers; per-token scales multiply S and P).  Key 500
+    of kv head 0 is planted as the largest e4m3 code with the sign of each
+    element of query row 150, head 0.  Per-tensor scale (None): it scores ~86
+    in base 2 against the row's first tile (~3), past the 64 a bf16 P holds,
+    so the workgroup runs a second pass.  Per-token scales: with the key's own
+    scale (1.0) it scores ~51, held in one pass with p up to ~2^48; with that
+    scale x4 it scores ~205 and forces the second pass.  Outputs and LSE
+    match the oracle on auto, one-pass and split-3 paths."""
+    tok = token_scale_mult is not None
+    case = make_case(seqs=[(200, 600)], head_dim=256, num_q_heads=8, num_kv_heads=2,
+                     block_size=16, q_dtype="bf16", kv_dtype="e4m3fn", token_scales=tok,
+                     seed=403 if tok else 402)
+    q = oracle.decode(case["q"][150, 0], "bf16")
+    key = 500  # visible to query tokens 100.. (context 400)
+    blk = int(case["block_table"][0][key // 16])
+    case["k_cache"][blk, key % 16, 0] = np.where(q >= 0, 0x7E, 0xFE).astype(np.uint8)
+    if tok:
+        case["k_token_scales"][blk, key % 16, 0] *= np.float32(token_scale_mult)
+
+    def k_row(k):
+        b = int(case["block_table"][0][k // 16])
+        s = case["k_token_scales"][b, k % 16, 0] if tok else case["k_scale"]
+        return oracle.decode(case["k_cache"][b, k % 16, 0], "e4m3fn") * np.float64(s)
+
+    c2 = case["scale"] / math.log(2.0)
+    first = max(float(q @ k_row(k)) * c2 for k in range(32))
+    excess = float(q @ k_row(key)) * c2 - first
+    assert (excess > 64.0) == (token_scale_mult != 1.0), excess
+    ref, ref_lse = oracle.attention(**case)
+    dev = to_device(case)
+    for path, n in (("auto", 0), ("2d", 0), ("splitkv", 3)):
+        got, lse, plan = run(case, dev, path=path, n_part=n, lse=True)
+        assert plan.kernel == 1
+        label = f"d256-hold-fp8-{token_scale_mult}/{path}{n}"
         compare(case, got, ref, label=label)
         check_lse(lse, ref_lse, case=case, label=label)
 
