@@ -541,6 +541,23 @@ def test_d256_held_maximum_fp8_cache(token_scale_mult):
         check_lse(lse, ref_lse, case=case, label=label)
 
 
+@pytest.mark.parametrize("num_short", [40, 100, 4200])
+def test_large_block_sequence_search(num_short):
+    """Large-block launches that locate each workgroup's sequence by a search
+    over the query offsets (neither one block per sequence nor rank order: one
+    200-token chunk among 40, 100 or 4200 chunks of 1-3 tokens); every
+    sequence's rows match the oracle."""
+    rng = np.random.default_rng(7000 + num_short)
+    seqs = [(int(q), int(q + rng.integers(0, 48))) for q in rng.integers(1, 4, num_short)]
+    seqs.insert(num_short // 2, (200, 300))
+    case = make_case(seqs=seqs, head_dim=64, num_q_heads=8, num_kv_heads=1, block_size=16,
+                     q_dtype="f16", seed=7100 + num_short)
+    ref, _ = oracle.attention(**case)
+    got, _, plan = run(case, path="2d")
+    assert plan.kernel in (1, 2) and (plan.flags & 3) == 0, (plan.kernel, plan.flags)
+    compare(case, got, ref, label=f"seq-search-{num_short}")
+
+
 def test_nan_workspace_not_read():
     case, ref, _ = _workload("fp8kv_decode_b8_ctx6700_w4096")
     dev = _dev("fp8kv_decode_b8_ctx6700_w4096")
