@@ -506,7 +506,8 @@ def test_d256_held_maximum_fp8_cache(token_scale_mult):
     (staged through registers; per-token scales multiply S and P).  Key 500
     of kv head 0 is planted as the largest e4m3 code with the sign of each
     element of query row 150, head 0.  Per-tensor scale (None): it scores ~86
-    in base 2 against the row's first tile (~3), past the 64 a bf16 P holds,
+    in base 2 against the row's first tile (the one holding its diagonal,
+    ~3), past the 64 a bf16 P holds,
     so the workgroup runs a second pass.  Per-token scales: with the key's own
     scale (1.0) it scores ~51, held in one pass with p up to ~2^48; with that
     scale x4 it scores ~205 and forces the second pass.  Outputs and LSE
@@ -527,8 +528,11 @@ def test_d256_held_maximum_fp8_cache(token_scale_mult):
         s = case["k_token_scales"][b, k % 16, 0] if tok else case["k_scale"]
         return oracle.decode(case["k_cache"][b, k % 16, 0], "e4m3fn") * np.float64(s)
 
+    # The kernel walks each range backwards from the tile holding the diagonal:
+    # row 150 (position 550) first sees keys 544..550 of the 32-key tile 544.
     c2 = case["scale"] / math.log(2.0)
-    first = max(float(q @ k_row(k)) * c2 for k in range(32))
+    pos = 400 + 150
+    first = max(float(q @ k_row(k)) * c2 for k in range(pos - pos % 32, pos + 1))
     excess = float(q @ k_row(key)) * c2 - first
     assert (excess > 64.0) == (token_scale_mult != 1.0), excess
     ref, ref_lse = oracle.attention(**case)
