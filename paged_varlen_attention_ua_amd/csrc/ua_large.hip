@@ -476,15 +476,18 @@ __global__ __launch_bounds__(64 * NW, (large_min_groups<D, NW, FP8 && TS>())) vo
 
   const int ntiles = (k1 - k0 + TK - 1) / TK;
   // First key of the t-th tile a workgroup walks.  With the held maximum
-  // (head dim 256) the range is walked backwards, from the tile holding the
-  // diagonal: each row's maximum then comes from its nearest keys, which
-  // ALiBi (or any bias growing toward the query) scores highest, so later
-  // tiles rarely exceed it.  Walked forwards, an ALiBi row's first (farthest)
-  // tile sat hundreds of base-2 units below its last and sent nearly every
-  // workgroup through the second pass (measured on MI355X, 8k prompt with
-  // ALiBi: 2.48 ms against 1.87 for the rescaling kernel).
+  // (head dim 256) or ALiBi the range is walked backwards, from the tile
+  // holding the diagonal: each row's maximum then comes from its nearest keys,
+  // which ALiBi (or any bias growing toward the query) scores highest, so
+  // later tiles rarely exceed it.  Walked forwards, an ALiBi row's first
+  // (farthest) tile sat hundreds of base-2 units below its last: at head dim
+  // 256 nearly every workgroup ran the second pass (measured on MI355X, 8k
+  // prompt with ALiBi: 2.48 ms against 1.87 for the rescaling kernel; 1.25
+  // backwards), and below it the running maximum moved on most tiles (8k
+  // prompt at head dim 128 with ALiBi: 4.5% slower than backwards).
+  const bool backwards = kHold || p.alibi != nullptr;
   auto tile_key = [&](int t) __attribute__((always_inline)) -> int {
-    return kHold ? k0 + (ntiles - 1 - t) * TK : k0 + t * TK;
+    return backwards ? k0 + (ntiles - 1 - t) * TK : k0 + t * TK;
   };
 
   // Eight-wave groups (16-bit caches, plain logits: no softcap, ALiBi,
