@@ -476,18 +476,15 @@ __global__ __launch_bounds__(64 * NW, (large_min_groups<D, NW, FP8 && TS>())) vo
 
   const int ntiles = (k1 - k0 + TK - 1) / TK;
   // First key of the t-th tile a workgroup walks.  With the held maximum
-  // (head dim 256) or ALiBi the range is walked backwards, from the tile
-  // holding the diagonal: each row's maximum then comes from its nearest keys,
-  // which ALiBi (or any bias growing toward the query) scores highest, so
-  // later tiles rarely exceed it.  Walked forwards, an ALiBi row's first
-  // (farthest) tile sat hundreds of base-2 units below its last: at head dim
-  // 256 nearly every workgroup ran the second pass (measured on MI355X, 8k
-  // prompt with ALiBi: 2.48 ms against 1.87 for the rescaling kernel; 1.25
-  // backwards), and below it the running maximum moved on most tiles (8k
-  // prompt at head dim 128 with ALiBi: 4.5% slower than backwards).
-  const bool backwards = kHold || p.alibi != nullptr;
+  // (head dim 256) the range is walked backwards, from the tile holding the
+  // diagonal: each row's maximum then comes from its nearest keys, which
+  // ALiBi (or any bias growing toward the query) scores highest, so later
+  // tiles rarely exceed it.  Walked forwards, an ALiBi row's first (farthest)
+  // tile sat hundreds of base-2 units below its last and sent nearly every
+  // workgroup through the second pass (measured on MI355X, 8k prompt with
+  // ALiBi: 2.48 ms against 1.87 for the rescaling kernel; 1.25 backwards).
   auto tile_key = [&](int t) __attribute__((always_inline)) -> int {
-    return backwards ? k0 + (ntiles - 1 - t) * TK : k0 + t * TK;
+    return kHold ? k0 + (ntiles - 1 - t) * TK : k0 + t * TK;
   };
 
   // Eight-wave groups (16-bit caches, plain logits: no softcap, ALiBi,
@@ -882,7 +879,7 @@ __global__ __launch_bounds__(64 * NW, (large_min_groups<D, NW, FP8 && TS>())) vo
       if (copy) issue_copy(kbuf(NB{}), vbuf(NB{}), sTab[NB::value]);
     }
     const bool filler = t + NBUF < ntiles && wave == (t & (NW - 1));
-    if (filler) fill_tab(sTab[B], tile_key(t + NBUF));
+    if (filler) fill_tab(sTab[B], kHold ? tile_key(t + NBUF) : kt + NBUF * TK);
     if (wave_live) compute(kbuf(bufc), vbuf(bufc), kt, &sSc[tsc ? t % tsc_lds<tsc>() : 0][0][0]);
     if constexpr (FP8) {
       if (copy) stage_store(kbuf(NB{}), vbuf(NB{}));
