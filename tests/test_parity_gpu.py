@@ -500,6 +500,22 @@ def test_d256_held_maximum_second_pass(q_dtype, factor):
         check_lse(lse, ref_lse, case=case, label=label)
 
 
+@pytest.mark.parametrize("q_dtype", ["bf16", "f16"])
+def test_d256_prefill_features(q_dtype):
+    """Head dim 256 prefill (four-wave groups: held running maximum, key ranges
+    walked backwards from the diagonal) with a window that starts mid-tile,
+    softcap with sinks, ALiBi (alone and with window and sinks) and QQ-bias,
+    one pass and split."""
+    seqs = [(200, 700), (37, 37), (90, 400)]
+    for i, kw in enumerate([dict(window=100), dict(softcap=20.0, sinks=True), dict(alibi=True),
+                            dict(alibi=True, window=70, sinks=True), dict(qq_bias=256)]):
+        case = make_case(seqs=seqs, seed=160 + i,
+                         **dict(BASE, head_dim=256, num_q_heads=8, q_dtype=q_dtype), **kw)
+        for path, n_part in (("2d", 0), ("splitkv", 3)):
+            _, plan = _check(case, path, n_part, label=f"d256-{q_dtype}-{i}-{path}{n_part}")
+            assert plan.kernel == 1
+
+
 @pytest.mark.parametrize("token_scale_mult", [None, 1.0, 4.0])
 def test_d256_held_maximum_fp8_cache(token_scale_mult):
     """The held maximum of the head-dim-256 prefill kernel with fp8 caches
