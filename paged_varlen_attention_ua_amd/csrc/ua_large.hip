@@ -985,6 +985,25 @@ __global__ __launch_bounds__(64 * NW, (large_min_groups<D, NW, FP8 && TS>())) vo
         if (t + 1 < ntiles) end_interval(2 * t + 2);
       }
     }
+  } else if constexpr (!FP8) {
+    auto run = [&]() __attribute__((always_inline)) {
+      for (int t = 0; t < ntiles; t += NBUF) {
+        step(I0{}, t);
+        if (t + 1 < ntiles) step(I1{}, t + 1);
+        if constexpr (NBUF > 2) {
+          if (t + 2 < ntiles) step(I2{}, t + 2);
+          if (t + 3 < ntiles) step(I3{}, t + 3);
+        }
+      }
+    };
+    // 16-bit caches: one copy of the loop per value of the uniform flag; in
+    // each the compiler drops the other branch of the logit code, which
+    // otherwise splits the tile's scheduling regions.  (fp8 kernels, whose
+    // staging holds more registers, spilled with two copies.)
+    if (general)
+      run();
+    else
+      run();
   } else {
     for (int t = 0; t < ntiles; t += NBUF) {
       step(I0{}, t);
