@@ -985,7 +985,7 @@ __global__ __launch_bounds__(64 * NW, (large_min_groups<D, NW, FP8 && TS>())) vo
         if (t + 1 < ntiles) end_interval(2 * t + 2);
       }
     }
-  } else if constexpr (!FP8) {
+  } else if constexpr (!(FP8 && TS)) {
     auto run = [&]() __attribute__((always_inline)) {
       for (int t = 0; t < ntiles; t += NBUF) {
         step(I0{}, t);
@@ -996,10 +996,10 @@ __global__ __launch_bounds__(64 * NW, (large_min_groups<D, NW, FP8 && TS>())) vo
         }
       }
     };
-    // 16-bit caches: one copy of the loop per value of the uniform flag; in
-    // each the compiler drops the other branch of the logit code, which
-    // otherwise splits the tile's scheduling regions.  (fp8 kernels, whose
-    // staging holds more registers, spilled with two copies.)
+    // One copy of the loop per value of the uniform flag; in each the
+    // compiler drops the other branch of the logit code, which otherwise
+    // splits the tile's scheduling regions.  (fp8 kernels with per-token
+    // scales, whose staging holds more registers, spilled with two copies.)
     // Head dims <= 128 split the featured copy once more, by softcap (ALiBi
     // or QQ-bias alone then skip the tanh branch: mixed fp16 batch with ALiBi
     // 15.4 -> 14.6 µs); at head dim 256 that third copy cost the plain one 1%.
