@@ -768,15 +768,13 @@ __global__ __launch_bounds__(64 * NW, (large_min_groups<D, NW, FP8 && TS>())) vo
           if constexpr (tsc) {
             psum += a + b;
             pop[kk][q] = pack2<QT>(a * v4[q >> 1][2 * (q & 1)], b * v4[q >> 1][2 * (q & 1) + 1]);
-          } else if constexpr (kHold) {
-            // Normalise by the sum of p as rounded for the PV MFMA: with a held
-            // maximum the dominant keys' p are far from 1, and dividing their
-            // rounded weights by an unrounded sum would cost up to 2^-9 of O.
+          } else {
+            // Normalise by the sum of p as rounded for the PV MFMA: O is then a
+            // weighted mean of V rows, so a row whose weight sits on a few keys
+            // loses nothing to the rounding of their p (dividing their rounded
+            // weights by an unrounded sum would cost up to 2^-9 of max |V|).
             pop[kk][q] = pack2<QT>(a, b);
             psum = add_pair<QT>(pop[kk][q], psum);
-          } else {
-            psum += a + b;
-            pop[kk][q] = pack2<QT>(a, b);
           }
         }
       }

@@ -500,6 +500,23 @@ def test_d256_held_maximum_second_pass(q_dtype, factor):
         check_lse(lse, ref_lse, case=case, label=label)
 
 
+@pytest.mark.parametrize("D", [64, 128])
+@pytest.mark.parametrize("kvd", ["bf16", "e4m3fn"])
+def test_four_wave_logit_forms(D, kvd):
+    """The four-wave prefill kernel runs one tile loop per logit form (plain;
+    ALiBi or QQ-bias without softcap; softcap): each form at head dims 64 and
+    128, 16-bit and per-tensor fp8 caches, one pass and split."""
+    seqs = [(150, 600), (37, 37), (70, 300)]
+    forms = [dict(), dict(alibi=True), dict(qq_bias=256, window=90), dict(softcap=15.0),
+             dict(softcap=15.0, alibi=True, sinks=True)]
+    for i, kw in enumerate(forms):
+        case = make_case(seqs=seqs, seed=170 + i,
+                         **dict(BASE, head_dim=D, kv_dtype=kvd, q_dtype="bf16"), **kw)
+        for path, n_part in (("2d", 0), ("splitkv", 2)):
+            _, plan = _check(case, path, n_part, label=f"fw-D{D}-{kvd}-{i}-{path}{n_part}")
+            assert plan.kernel == 1
+
+
 @pytest.mark.parametrize("q_dtype", ["bf16", "f16"])
 def test_d256_prefill_features(q_dtype):
     """Head dim 256 prefill (four-wave groups: held running maximum, key ranges
