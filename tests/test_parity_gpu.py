@@ -517,19 +517,20 @@ def test_four_wave_logit_forms(D, kvd):
             assert plan.kernel == 1
 
 
-@pytest.mark.parametrize("q_dtype", ["bf16", "f16"])
-def test_d256_prefill_features(q_dtype):
+@pytest.mark.parametrize("q_dtype,kvd", [("bf16", "bf16"), ("f16", "f16"), ("bf16", "e4m3fn")])
+def test_d256_prefill_features(q_dtype, kvd):
     """Head dim 256 prefill (four-wave groups: held running maximum, key ranges
     walked backwards from the diagonal) with a window that starts mid-tile,
     softcap with sinks, ALiBi (alone and with window and sinks) and QQ-bias,
-    one pass and split."""
+    16-bit and per-tensor fp8 caches, one pass and split."""
     seqs = [(200, 700), (37, 37), (90, 400)]
     for i, kw in enumerate([dict(window=100), dict(softcap=20.0, sinks=True), dict(alibi=True),
                             dict(alibi=True, window=70, sinks=True), dict(qq_bias=256)]):
         case = make_case(seqs=seqs, seed=160 + i,
-                         **dict(BASE, head_dim=256, num_q_heads=8, q_dtype=q_dtype), **kw)
+                         **dict(BASE, head_dim=256, num_q_heads=8, q_dtype=q_dtype,
+                                kv_dtype=kvd), **kw)
         for path, n_part in (("2d", 0), ("splitkv", 3)):
-            _, plan = _check(case, path, n_part, label=f"d256-{q_dtype}-{i}-{path}{n_part}")
+            _, plan = _check(case, path, n_part, label=f"d256-{q_dtype}-{kvd}-{i}-{path}{n_part}")
             assert plan.kernel == 1
 
 
